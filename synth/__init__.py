@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs (weights as packed super-blocks, fp32 activations).
+
+This module is the one input source that both the oracle side and the HIP side
+use. It holds none of the product's arithmetic: bytes 4..143 of every 144-byte
+super-block are uniform random bytes, so each 6-bit scale, 6-bit min and 4-bit
+quant inside them is uniform over its range whatever the packing; bytes 0..3
+are the binary16 values d and dmin = f16(|z|*1e-2). Activations are
+f32(scale*z), z ~ N(0,1). The streams are counter-based SplitMix64 (Steele, Lea
+and Flood, OOPSLA 2014) keyed by (seed, tensor id, field), so every value is a
+pure function of its index and the output does not depend on the thread count.
+
+Workload: synthetic stand-ins for the Q4_K_M GGUF weights and the activations
+of the 27B model on "sixi-asi 0.9" (section "Numbers"); no trained weights are
+used.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+
+DEFAULT_SEED = 20261202
+BLOCK_BYTES = 144
+BLOCK_WEIGHTS = 256
+FIELD_BYTES, FIELD_D, FIELD_DMIN, FIELD_X = 1, 2, 3, 4
+
+
+def build():
+    """Compile synth.c into libsynth.so (gcc, OpenMP)."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99",
+                           "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.synth_weights.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_weights.restype = ctypes.c_int
+        lib.synth_acts.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_double, ctypes.c_void_p]
+        lib.synth_acts.restype = ctypes.c_int
+        lib.synth_f64_to_f16.argtypes = [ctypes.c_double]
+        lib.synth_f64_to_f16.restype = ctypes.c_uint16
+        lib.synth_word.argtypes = [ctypes.c_uint64] * 4
+        lib.synth_word.restype = ctypes.c_uint64
+        lib.synth_normal.argtypes = [ctypes.c_uint64] * 4
+        lib.synth_normal.restype = ctypes.c_double
+        lib.synth_threads.argtypes = []
+        lib.synth_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def weight_bytes(n_rows, K):
+    return int(n_rows) * (int(K) // BLOCK_WEIGHTS) * BLOCK_BYTES
+
+
+def weights(n_rows, K, tensor, seed=DEFAULT_SEED, out=None):
+    """Packed super-blocks for an n_rows x K matrix: uint8 array [n_rows, K/256*144]."""
+    if K <= 0 or K % BLOCK_WEIGHTS:
+        raise ValueError("K must be a positive multiple of 256")
+    shape = (int(n_rows), int(K) // BLOCK_WEIGHTS * BLOCK_BYTES)
+    if out is None:
+        out = np.empty(shape, dtype=np.uint8)
+    assert out.dtype == np.uint8 and out.flags.c_contiguous and out.size == shape[0] * shape[1]
+    rc = _load().synth_weights(seed, tensor, int(n_rows), int(K), out.ctypes.data)
+    if rc:
+        raise RuntimeError("synth_weights failed")
+    return out
+
+
+def acts(M, K, tensor, seed=DEFAULT_SEED, scale=1.0, out=None):
+    """fp32 activations [M, K], x = f32(scale * z), z ~ N(0,1)."""
+    if out is None:
+        out = np.empty((int(M), int(K)), dtype=np.float32)
+    assert out.dtype == np.float32 and out.flags.c_contiguous and out.size == M * K
+    rc = _load().synth_acts(seed, tensor, int(M), int(K), float(scale), out.ctypes.data)
+    if rc:
+        raise RuntimeError("synth_acts failed")
+    return out
+
+
+def f64_to_f16_bits(v):
+    return int(_load().synth_f64_to_f16(float(v)))
+
+
+def word(seed, tensor, field, i):
+    return int(_load().synth_word(seed, tensor, field, i))
+
+
+def normal(seed, tensor, field, i):
+    return float(_load().synth_normal(seed, tensor, field, i))
+
+
+def threads():
+    return int(_load().synth_threads())
