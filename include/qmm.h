@@ -1,0 +1,157 @@
+/*
+ * qmm.h -- C ABI of the skinny quantized matrix product on MI355X (gfx950).
+ *
+ *   y[M,N] = x[M,K] . dequant(W)[N,K]^T
+ *
+ * for skinny batches M = 1..32, where W is stored as 4.5-bit k-quant
+ * super-blocks (Q4_K). This is the product that takes the time of a
+ * speculative-decoding verify pass:
+ *   - "sixi-asi 0.9", section "What I got wrong in 0.8": a verify step runs
+ *     the target model over the anchor plus k drafts in one batched pass, and
+ *     quantized matrix products take 83-92% of its GPU time; the per-row cost
+ *     came from a kernel that decoded the 4-bit weights again for every row.
+ *   - "sixi-asi 0.11", section "Why sixteen streams were the ceiling": several
+ *     streams share one pass, and the pass reads the whole weight set once
+ *     almost regardless of the number of rows (up to 32 streams).
+ *   - "sixi-asi 0.9", section "The patch": the switch point between the
+ *     row-vector and the tiled kernel and the occupancy of the tiled kernel
+ *     decide the time; a time faster than reading the weights at full memory
+ *     bandwidth is a bug, not a result.
+ *
+ * Weight format (one super-block = 256 consecutive weights along K, 144 bytes;
+ * the Q4_K k-quant of the Q4_K_M GGUF files named in "sixi-asi 0.9", section
+ * "Numbers"; the byte map is the public Q4_K layout):
+ *   bytes 0..1   d     binary16, little-endian
+ *   bytes 2..3   dmin  binary16, little-endian
+ *   bytes 4..15  eight 6-bit scales sc_j and eight 6-bit mins m_j, packed:
+ *                j < 4:  sc_j = s[j] & 63,  m_j = s[j+4] & 63
+ *                j >= 4: sc_j = (s[j+4] & 15) | (s[j-4] >> 6) << 4
+ *                        m_j  = (s[j+4] >> 4) | (s[j]   >> 6) << 4
+ *   bytes 16..143 quants: weight 64c + r (c = 0..3, r = 0..63) is the low
+ *                nibble (r < 32) or high nibble (r >= 32) of byte
+ *                16 + 32c + (r mod 32)
+ *   weight i of the block: w = d * sc_j * q_i - dmin * m_j,  j = i / 32.
+ * A matrix W[N,K] is N rows of K/256 consecutive blocks; rows are consecutive.
+ * Block (n, b) starts at byte (n * (K/256) + b) * 144.
+ *
+ * Numerics: fp32 output. Activations are rounded once to binary16 inside the
+ * kernels (the same rounded value feeds the quant term and the min term), the
+ * products of quants and scales are exact, and all sums are fp32. Per element
+ * |y - y_exact| <= 2e-3 * sum_k |w[n,k] * x[m,k]| holds for |x| < 65504 (the
+ * binary16 range). The summation order is fixed by the launch plan, so repeated
+ * calls with the same plan give bit-identical results.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. 0 is success; every error is negative and no kernel is
+ * launched when a call returns an error. */
+enum {
+  QMM_OK = 0,
+  QMM_ERR_INVALID_ARG = -1, /* null handle/pointer, bad override values */
+  QMM_ERR_SHAPE = -2,       /* M outside 1..32, N < 1, K < 256 or K % 256 != 0 */
+  QMM_ERR_ALIGN = -3,       /* x or W_blocks not 16-byte aligned, y not 4-byte aligned */
+  QMM_ERR_NO_DEVICE = -4,   /* device index invalid or not gfx950 */
+  QMM_ERR_OOM = -5,         /* workspace allocation failed in qmm_create */
+  QMM_ERR_HIP = -6,         /* a HIP runtime call or a launch failed */
+  QMM_ERR_OVERLAP = -7      /* y overlaps x or W_blocks */
+};
+
+/* Largest batch (rows of x) a call accepts: one row per stream for up to 32
+ * concurrent streams ("sixi-asi 0.11", table and section "Why sixteen streams
+ * were the ceiling"). */
+#define QMM_MAX_M 32
+
+typedef struct qmm_ctx* qmm_handle;
+
+/* Create a handle on HIP device `device`. Queries the device (CU count, LDS,
+ * architecture; only gfx950 is accepted), loads the launch table and allocates
+ * the split-K workspace: 128 MiB of partial sums and 4 MiB of per-tile arrival
+ * counters (device memory owned by the handle; the counters are zeroed here,
+ * synchronously). device == -1 creates a planning-only handle: it plans and
+ * checks arguments but never launches (qmm_run then returns
+ * QMM_ERR_NO_DEVICE after its argument checks). On error *out is set to NULL.
+ * A handle may be used by one stream at a time; create one handle per
+ * concurrent stream. */
+int qmm_create(qmm_handle* out, int device);
+
+/* y = x . dequant(W_blocks)^T, enqueued on `stream`; returns at once and never
+ * synchronizes.
+ *   x        device pointer, fp32 [M][K] row-major, 16-byte aligned.
+ *   W_blocks device pointer, N*K/256 super-blocks of 144 bytes in the layout
+ *            above, 16-byte aligned.
+ *   y        device pointer, fp32 [M][N] row-major, 4-byte aligned; it is
+ *            overwritten (not accumulated into) and must not overlap x or W.
+ *   M in 1..QMM_MAX_M, N >= 1, K >= 256 with K % 256 == 0.
+ * All three buffers are owned by the caller, who keeps them alive until the
+ * stream work completes; the library never frees or retains them. The pointers
+ * must be on the handle's device (not checked). Argument errors are returned
+ * before anything is launched; faults inside a kernel surface at the caller's
+ * next synchronization. */
+int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y,
+            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* Free the handle and its workspace. qmm_destroy(NULL) is a no-op returning
+ * QMM_OK. The caller must make sure no work enqueued with the handle is still
+ * running. */
+int qmm_destroy(qmm_handle h);
+
+/* Static, human-readable text for a status code. */
+const char* qmm_status_string(int status);
+
+/* Weight bytes of an N x K matrix in this format: 144 * N * K / 256 (the
+ * weight-only byte count behind every bandwidth figure; "sixi-asi 0.9",
+ * section "The patch": 15.8 GB per pass at 273 GB/s is the ~58 ms floor).
+ * Returns 0 for invalid shapes. */
+uint64_t qmm_weight_bytes(int64_t N, int64_t K);
+
+/* Kernels of the launch table. */
+enum {
+  QMM_KERNEL_AUTO = 0,  /* let the launch table decide (for overrides) */
+  QMM_KERNEL_VECTOR = 1, /* row-vector kernel: VALU dot products, x broadcast */
+  QMM_KERNEL_TILED = 2   /* tiled kernel: MFMA 16x16x32 f16, M >= 8 only */
+};
+
+/* One launch-table entry: which kernel, how the grid is shaped. */
+typedef struct {
+  int32_t kernel;        /* QMM_KERNEL_VECTOR or QMM_KERNEL_TILED */
+  int32_t waves_per_wg;  /* wavefronts per workgroup: 1, 2, 4 or 8 */
+  int32_t splits;        /* K split into this many slices (1 = no split-K) */
+  int32_t grid_x;        /* workgroups per K slice (one 16-row tile per wavefront) */
+  int32_t blocks_per_split; /* super-blocks along K per slice */
+  int32_t lds_bytes;     /* LDS per workgroup */
+  int64_t workspace_bytes; /* split-K partials used (0 when splits == 1) */
+} qmm_plan;
+
+/* The entry qmm_run would use for (M, N, K) with the handle's current
+ * overrides. Returns a status like qmm_run's argument checks. */
+int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out);
+
+/* Force a kernel for every following call on this handle (QMM_KERNEL_AUTO
+ * restores the table). QMM_KERNEL_TILED with M < 8 makes qmm_run return
+ * QMM_ERR_INVALID_ARG. For tests and sweeps. */
+int qmm_set_kernel(qmm_handle h, int kernel);
+
+/* Override the grid shape for every following call: waves_per_wg (0 = table),
+ * splits (0 = table), grid_x (0 = table; otherwise at least the number of
+ * workgroups the call needs, one 16-row tile per wavefront). Values that do
+ * not fit the call (LDS, workspace, K, grid) make qmm_run return
+ * QMM_ERR_INVALID_ARG. For sweeps. */
+int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x);
+
+/* The row count from which the launch table switches from the row-vector to
+ * the tiled kernel (M >= switch uses the tiled kernel; never below 8). */
+int qmm_switch_point(qmm_handle h, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

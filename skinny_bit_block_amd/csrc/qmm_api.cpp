@@ -1,0 +1,270 @@
+// C ABI of the skinny quantized product: argument checks, the gfx950 launch
+// table, the split-K workspace and the launch on the caller's stream.
+//
+// The launch table plays the role of the per-architecture switch tables of the
+// pages ("sixi-asi 0.9", sections "What I got wrong in 0.8" and "The patch"):
+// the row count at which the row-vector kernel hands over to the tiled kernel,
+// and the launch shape (waves per workgroup, split-K) that keeps enough loads
+// in flight. A wrong entry there cost the pages' 8-row pass 163 vs 88 ms.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+struct qmm_ctx {
+  int device;           // -1: planning-only handle (no device, no workspace)
+  int cus;              // compute units
+  int forced_kernel;    // QMM_KERNEL_*
+  int force_waves, force_splits, force_grid;
+  float* ws;            // split-K partials
+  int64_t ws_bytes;
+  unsigned* counters;   // split-K arrival counters, one per row tile, zeroed at creation
+};
+
+namespace {
+
+constexpr int64_t kWorkspaceBytes = 128ll << 20;
+constexpr int kGfx950Cus = 256;
+constexpr int kDefaultWaves = 4;
+// Split K until there are at least this many row tiles of work (a wave per
+// tile); below that the chip cannot keep enough loads in flight.
+constexpr int64_t kTargetTiles = 2048;
+constexpr int kMinBlocksPerSlice = 4;
+
+int check_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > QMM_MAX_M || N < 1 || N > (int64_t)INT32_MAX / 32 || K < 256 ||
+      K % 256 != 0 || K > (int64_t)1 << 24)
+    return QMM_ERR_SHAPE;
+  return QMM_OK;
+}
+
+int table_switch(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return 8;
+}
+
+int make_plan(const qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
+  int rc = check_shape(M, N, K);
+  if (rc) return rc;
+  const int nb = (int)(K / 256);
+  const int64_t ntiles = (N + 15) / 16;
+  int kernel = M >= table_switch(N, K) ? QMM_KERNEL_TILED : QMM_KERNEL_VECTOR;
+  if (h->forced_kernel != QMM_KERNEL_AUTO) kernel = h->forced_kernel;
+  if (kernel == QMM_KERNEL_TILED && M < 8) return QMM_ERR_INVALID_ARG;
+
+  const int waves = h->force_waves ? h->force_waves : kDefaultWaves;
+  if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return QMM_ERR_INVALID_ARG;
+
+  int splits;
+  if (h->force_splits) {
+    splits = h->force_splits;
+    if (splits < 1 || splits > nb) return QMM_ERR_INVALID_ARG;
+  } else {
+    // fewest slices whose activations fit in LDS ...
+    int s_lds = 1;
+    while (s_lds < nb && qmm::lds_bytes((int)M, (nb + s_lds - 1) / s_lds, waves) > qmm::kLdsMax) ++s_lds;
+    // ... and enough row-tile work items to fill the chip, keeping at least a
+    // ring's worth of super-blocks per slice
+    int s_par = 1;
+    while (ntiles * s_par < kTargetTiles && (nb + s_par) / (s_par + 1) >= kMinBlocksPerSlice &&
+           ntiles <= qmm::kMaxCounterTiles)
+      ++s_par;
+    splits = s_lds > s_par ? s_lds : s_par;
+  }
+  const int nbs = (nb + splits - 1) / splits;
+  splits = (nb + nbs - 1) / nbs;  // no empty slice
+  const int lds = qmm::lds_bytes((int)M, nbs, waves);
+  if (lds > qmm::kLdsMax) return QMM_ERR_INVALID_ARG;
+  const int64_t ws = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+  if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
+  if (splits > 1 && ntiles > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
+
+  // one row tile per wavefront
+  const int64_t need = (ntiles + waves - 1) / waves;
+  int64_t grid = need;
+  if (h->force_grid) {
+    if (h->force_grid < need) return QMM_ERR_INVALID_ARG;
+    grid = h->force_grid;
+  }
+  if (grid > 0x7FFFFFFF) return QMM_ERR_INVALID_ARG;
+
+  p->kernel = kernel;
+  p->waves_per_wg = waves;
+  p->splits = splits;
+  p->grid_x = (int32_t)grid;
+  p->blocks_per_split = nbs;
+  p->lds_bytes = lds;
+  p->workspace_bytes = ws;
+  return QMM_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmm_status_string(int status) {
+  switch (status) {
+    case QMM_OK: return "QMM_OK";
+    case QMM_ERR_INVALID_ARG: return "QMM_ERR_INVALID_ARG: null pointer or handle, or an override that does not fit the call";
+    case QMM_ERR_SHAPE: return "QMM_ERR_SHAPE: need 1 <= M <= 32, N >= 1, K >= 256 and K % 256 == 0";
+    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: x and W_blocks must be 16-byte aligned, y 4-byte aligned";
+    case QMM_ERR_NO_DEVICE: return "QMM_ERR_NO_DEVICE: no usable gfx950 device";
+    case QMM_ERR_OOM: return "QMM_ERR_OOM: workspace allocation failed";
+    case QMM_ERR_HIP: return "QMM_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case QMM_ERR_OVERLAP: return "QMM_ERR_OVERLAP: y overlaps x or W_blocks";
+    default: return "QMM: unknown status";
+  }
+}
+
+uint64_t qmm_weight_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || K % 256 != 0) return 0;
+  return (uint64_t)N * (uint64_t)(K / 256) * 144u;
+}
+
+int qmm_create(qmm_handle* out, int device) {
+  if (!out) return QMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  qmm_ctx* h = new (std::nothrow) qmm_ctx();
+  if (!h) return QMM_ERR_OOM;
+  h->device = device;
+  h->cus = kGfx950Cus;
+  h->forced_kernel = QMM_KERNEL_AUTO;
+  h->ws = nullptr;
+  h->ws_bytes = kWorkspaceBytes;
+  h->counters = nullptr;
+  if (device == -1) {  // planning-only handle
+    *out = h;
+    return QMM_OK;
+  }
+  int count = 0;
+  if (device < 0 || hipGetDeviceCount(&count) != hipSuccess || device >= count) {
+    delete h;
+    return QMM_ERR_NO_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess ||
+      std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    delete h;
+    return QMM_ERR_NO_DEVICE;
+  }
+  h->cus = prop.multiProcessorCount;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) {
+    delete h;
+    return QMM_ERR_HIP;
+  }
+  const char* inject = std::getenv("QMM_TEST_FAIL_ALLOC");  // failure-injection hook for tests
+  hipError_t e = hipSuccess;
+  if (!(inject && inject[0] == '1')) e = hipMalloc(reinterpret_cast<void**>(&h->ws), (size_t)h->ws_bytes);
+  if (inject && inject[0] == '1') h->ws = nullptr;
+  if (e == hipSuccess && h->ws)
+    e = hipMalloc(reinterpret_cast<void**>(&h->counters), qmm::kMaxCounterTiles * sizeof(unsigned));
+  if (e != hipSuccess || !h->ws || !h->counters) {
+    (void)hipGetLastError();
+    if (h->ws) (void)hipFree(h->ws);
+    (void)hipSetDevice(prev);
+    delete h;
+    return QMM_ERR_OOM;
+  }
+  // the counters start at zero; every split-K call leaves them at zero
+  e = hipMemset(h->counters, 0, qmm::kMaxCounterTiles * sizeof(unsigned));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = qmm::prepare_kernels();
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) {
+    (void)hipFree(h->ws);
+    (void)hipFree(h->counters);
+    delete h;
+    return QMM_ERR_HIP;
+  }
+  *out = h;
+  return QMM_OK;
+}
+
+int qmm_destroy(qmm_handle h) {
+  if (!h) return QMM_OK;
+  if (h->ws || h->counters) {
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(h->device);
+    if (h->ws) (void)hipFree(h->ws);
+    if (h->counters) (void)hipFree(h->counters);
+    (void)hipSetDevice(prev);
+  }
+  delete h;
+  return QMM_OK;
+}
+
+int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out) {
+  if (!h || !out) return QMM_ERR_INVALID_ARG;
+  return make_plan(h, M, N, K, out);
+}
+
+int qmm_set_kernel(qmm_handle h, int kernel) {
+  if (!h || kernel < QMM_KERNEL_AUTO || kernel > QMM_KERNEL_TILED) return QMM_ERR_INVALID_ARG;
+  h->forced_kernel = kernel;
+  return QMM_OK;
+}
+
+int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x) {
+  if (!h || waves_per_wg < 0 || splits < 0 || grid_x < 0) return QMM_ERR_INVALID_ARG;
+  h->force_waves = waves_per_wg;
+  h->force_splits = splits;
+  h->force_grid = grid_x;
+  return QMM_OK;
+}
+
+int qmm_switch_point(qmm_handle h, int64_t N, int64_t K) {
+  if (!h) return QMM_ERR_INVALID_ARG;
+  return table_switch(N, K);
+}
+
+int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_t M, int64_t N,
+            int64_t K, hipStream_t stream) {
+  if (!h || !x || !W_blocks || !y) return QMM_ERR_INVALID_ARG;
+  int rc = check_shape(M, N, K);
+  if (rc) return rc;
+  if (((uintptr_t)x & 15) || ((uintptr_t)W_blocks & 15) || ((uintptr_t)y & 3))
+    return QMM_ERR_ALIGN;
+  const size_t ybytes = (size_t)(M * N * 4);
+  if (overlaps(y, ybytes, x, (size_t)(M * K * 4)) ||
+      overlaps(y, ybytes, W_blocks, (size_t)qmm_weight_bytes(N, K)))
+    return QMM_ERR_OVERLAP;
+  qmm_plan p;
+  rc = make_plan(h, M, N, K, &p);
+  if (rc) return rc;
+  if (h->device < 0) return QMM_ERR_NO_DEVICE;
+
+  qmm::Launch a;
+  a.kernel = p.kernel;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.waves_per_wg = p.waves_per_wg;
+  a.splits = p.splits;
+  a.grid_x = p.grid_x;
+  a.nbs = p.blocks_per_split;
+  a.xs_m = qmm::lds_xs_m(p.blocks_per_split);
+  a.ss_m = qmm::lds_ss_m(p.blocks_per_split);
+  a.lds_bytes = p.lds_bytes;
+  a.x = x;
+  a.W = W_blocks;
+  a.y = y;
+  a.ws = h->ws;
+  a.counters = h->counters;
+  return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+}  // extern "C"

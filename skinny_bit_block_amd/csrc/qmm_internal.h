@@ -1,0 +1,57 @@
+// Internal interface between the host side (qmm_api.cpp) and the kernels
+// (qmm_kernels.hip) of the skinny quantized product library.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace qmm {
+
+constexpr int kBlockWeights = 256;  // weights per super-block (along K)
+constexpr int kBlockBytes = 144;    // bytes per super-block
+// LDS layout of the staged activations: one 16-byte unit per
+// (row m, super-block, j-pair g, dword t); a j-pair (two 32-weight
+// sub-blocks) is 8 units plus 16 bytes of padding, so the four j-pairs of a
+// block sit in different LDS banks.
+constexpr int kLdsPairStride = 144;
+constexpr int kLdsBlockStride = 4 * kLdsPairStride;
+constexpr int kLdsMax = 160 * 1024;  // LDS a workgroup may allocate on gfx950
+constexpr int kMaxWavesPerWg = 8;
+
+struct Launch {
+  int kernel;       // 1 = row-vector, 2 = tiled (MFMA)
+  int M, N, K;
+  int waves_per_wg;
+  int splits;       // K slices (grid.y)
+  int grid_x;       // workgroups per slice
+  int nbs;          // super-blocks per slice
+  int xs_m;         // LDS bytes per staged activation row
+  int ss_m;         // floats per row of staged sub-block sums
+  int lds_bytes;
+  const float* x;
+  const void* W;
+  float* y;
+  float* ws;        // split-K partials [splits][M][N] (splits > 1)
+  unsigned* counters;  // split-K arrival counter per row tile, zero between calls
+};
+
+// Row tiles a split-K call may have (one arrival counter each).
+constexpr int64_t kMaxCounterTiles = 1 << 20;
+
+// Per-row LDS strides for nbw staged super-blocks.
+inline int lds_xs_m(int nbw) {
+  // a row stride congruent to 64 mod 128 spreads the 16 rows an MFMA operand
+  // read touches over all banks
+  return nbw * kLdsBlockStride + ((nbw & 1) ? 0 : 64);
+}
+inline int lds_ss_m(int nbw) { return nbw * 8 + 2; }
+// Per-wavefront transpose buffer of the weight stream: 16 rows x (4 blocks =
+// 36 chunks of 16 B + one chunk of padding).
+constexpr int kWaveBufBytes = 16 * 16 * 37;
+inline int lds_bytes(int M, int nbw, int waves) {
+  return M * lds_xs_m(nbw) + M * lds_ss_m(nbw) * 4 + waves * kWaveBufBytes;
+}
+
+hipError_t launch(const Launch& a, hipStream_t stream);
+hipError_t prepare_kernels();  // raise the dynamic-LDS limit of every kernel
+
+}  // namespace qmm

@@ -1,0 +1,686 @@
+// HIP kernels (gfx950) of the skinny quantized product
+//   y[M,N] = x[M,K] . dequant(W)[N,K]^T,  M = 1..32,
+// W in 144-byte / 256-weight Q4_K super-blocks (layout in include/qmm.h).
+//
+// The pages' finding ("sixi-asi 0.9", section "What I got wrong in 0.8") is
+// that a kernel which decodes the 4-bit weights again for every row makes the
+// verify pass pay per row. Here every super-block is loaded once and
+// dequantized once, in registers, and that one decode serves all M rows.
+//
+// Work split, common to both kernels: a wavefront owns 16 consecutive rows n
+// (a row tile). Lane l = 16 g + r handles row r of the tile and the j-pair g
+// (sub-blocks 2g and 2g+1, i.e. weights 64g .. 64g+63 of each super-block):
+// it loads the block header (16 B) and the 32 quant bytes 32g .. 32g+31 with
+// 128-bit loads. Those bytes hold weights 64g+i (low nibble of byte i) and
+// 64g+32+i (high nibble). A row tile walks the super-blocks of its K slice in
+// ascending order; each workgroup first stages its K slice of x in LDS, rounded
+// once to binary16 and arranged to match the nibble order, together with the
+// fp32 sums of every 32-weight sub-block of the rounded x (the min term).
+//
+// Nibble unpack: masking a quant dword with 0x000F000F leaves two binary16
+// subnormals q*2^-24 (bytes 0 and 2, low nibbles); 0x00F000F0 leaves q*2^-20
+// (high nibbles); the same after a shift by 8 gives bytes 1 and 3. gfx950
+// keeps binary16 subnormals in v_dot2_f32_f16, v_pk_mul_f16 and the f16 MFMA,
+// so this is exact and needs no bias correction.
+//
+// Row-vector kernel (VALU): per row m, v_dot2_f32_f16 of the unpacked quants
+// with the staged x, two fp32 partial sums per lane (one per sub-block), then
+//   y += d*sc_a*2^24 * P_a + d*sc_b*2^20 * P_b - dmin*m_a*S_a - dmin*m_b*S_b.
+// Tiled kernel (MFMA): the quants are scaled by their sub-block scale with one
+// v_pk_mul_f16 per pair (q*sc*2^-14, exact: q*sc <= 945), the staged x is the
+// A operand and the weights the B operand of v_mfma_f32_16x16x32_f16, so a
+// lane's four outputs belong to its own row n and the per-block d is a lane
+// constant; the min term is a v_mfma_f32_16x16x4_f32 of the sub-block sums
+// with -dmin*m_j. Accumulation is fp32 in a fixed order in both kernels.
+// With split-K, every slice writes its partial sums, and the wave that
+// finishes a row tile last (an atomic arrival counter per tile) adds the
+// partials in slice order and writes y, then resets the counter for the next
+// call; which wave is last does not change the order of the sum, so results
+// are bit-identical from run to run for a given launch plan, and a call is a
+// single kernel launch. Every wave owns exactly one row tile of one K slice.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ uint32_t pk_mul(uint32_t a, h2_t s) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) * s);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// Header of a super-block, the part lane group g needs: d, dmin and the
+// scales/mins of sub-blocks 2g (a) and 2g+1 (b).
+struct Header {
+  float d, dmin;
+  uint32_t sc_a, sc_b, m_a, m_b;
+};
+
+// Per-lane constants of the header decode. The twelve packed scale bytes are
+// s0..s3 = h.y, s4..s7 = h.z, s8..s11 = h.w. Lane group g needs
+//   g < 2:  sc = s[2g], s[2g+1] (low 6 bits), m = s[4+2g], s[5+2g] (low 6 bits)
+//   g >= 2 (t = g-2): low 4 bits from s[8+2t], s[9+2t] (scale: low nibble,
+//          min: high nibble), bits 4..5 from the top two bits of s[2t], s[2t+1]
+//          (scale) and of s[4+2t], s[5+2t] (min).
+// One v_perm_b32 gathers the four low-part bytes, one gathers the four
+// high-part bytes, and per-lane masks finish the job: bytes [sc_a, sc_b, m_a, m_b].
+struct HeaderLane {
+  uint32_t sel_lo, mask_a, mask_b, sel_hi, mask_h;
+  bool hi_group;
+};
+
+__device__ __forceinline__ HeaderLane header_lane(int g) {
+  HeaderLane c;
+  const uint32_t t = (uint32_t)(g & 1) * 2u;
+  c.hi_group = g >= 2;
+  if (g < 2) {
+    c.sel_lo = t | ((t + 1) << 8) | ((4 + t) << 16) | ((5 + t) << 24);
+    c.mask_a = 0x3F3F3F3Fu;
+    c.mask_b = 0u;
+    c.sel_hi = 0x0C0C0C0Cu;  // selector 12 = zero byte
+    c.mask_h = 0u;
+  } else {
+    c.sel_lo = t | ((t + 1) << 8) | (t << 16) | ((t + 1) << 24);
+    c.mask_a = 0x00000F0Fu;
+    c.mask_b = 0x0F0F0000u;
+    c.sel_hi = t | ((t + 1) << 8) | ((4 + t) << 16) | ((5 + t) << 24);
+    c.mask_h = 0x30303030u;
+  }
+  return c;
+}
+
+// [sc_a, sc_b, m_a, m_b] as the four bytes of one dword.
+__device__ __forceinline__ uint32_t scale_bytes(u4_t h, const HeaderLane& c) {
+  const uint32_t s0 = c.hi_group ? h.w : h.z;
+  const uint32_t s1 = c.hi_group ? h.w : h.y;
+  uint32_t lo = __builtin_amdgcn_perm(s0, s1, c.sel_lo);
+  lo = (lo & c.mask_a) | ((lo >> 4) & c.mask_b);
+  const uint32_t hi = __builtin_amdgcn_perm(h.z, h.y, c.sel_hi);
+  return ((hi >> 2) & c.mask_h) | lo;
+}
+
+__device__ __forceinline__ Header decode_header(u4_t h, const HeaderLane& c) {
+  Header o;
+  o.d = f16_lo(h.x);
+  o.dmin = f16_hi(h.x);
+  const uint32_t b = scale_bytes(h, c);
+  o.sc_a = b & 0xFFu;
+  o.sc_b = (b >> 8) & 0xFFu;
+  o.m_a = (b >> 16) & 0xFFu;
+  o.m_b = b >> 24;
+  return o;
+}
+
+// Stage x[0..M)[K slice] into LDS: unit (m, bl, g, t) holds, as binary16
+// pairs, x at block offsets 64g + {4t, 4t+2 | 4t+1, 4t+3 | 32+4t, 32+4t+2 |
+// 32+4t+1, 32+4t+3}; sums[m][bl][j] is the fp32 sum of the rounded x over
+// sub-block j. The eight lanes t = 0..7 of a (m, bl, g) group are adjacent,
+// so the sub-block sums are a fixed xor-butterfly over those lanes.
+// A thread handles kStageBatch units per batch and issues all their loads
+// before it converts any; the first batch is issued before the weight ring,
+// so the latencies of x and of the first weights overlap.
+constexpr int kStageBatch = 4;
+
+struct StageBatch {
+  float4 lo[kStageBatch], hi[kStageBatch];
+};
+
+struct StageArgs {
+  const float* x;
+  int M, K, kb0, nbw, xs_m, ss_m;
+  char* lds_x;
+  float* lds_s;
+};
+
+__device__ __forceinline__ void stage_issue(const StageArgs& a, int base, StageBatch& b) {
+  const int nunits = a.M * a.nbw * 32;
+  const int nthr = (int)blockDim.x;
+#pragma unroll
+  for (int i = 0; i < kStageBatch; ++i) {
+    const int u = base + i * nthr + (int)threadIdx.x;
+    const int uu = u < nunits ? u : 0;
+    const int t = uu & 7, g = (uu >> 3) & 3, rest = uu >> 5;
+    const int bl = rest % a.nbw, m = rest / a.nbw;
+    const float* src =
+        a.x + (size_t)m * a.K + (size_t)(a.kb0 + bl) * kBlockWeights + 64 * g + 4 * t;
+    b.lo[i] = *reinterpret_cast<const float4*>(src);
+    b.hi[i] = *reinterpret_cast<const float4*>(src + 32);
+  }
+}
+
+__device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const StageBatch& b) {
+  const int nunits = a.M * a.nbw * 32;
+  const int nthr = (int)blockDim.x;
+#pragma unroll
+  for (int i = 0; i < kStageBatch; ++i) {
+    if (base + i * nthr >= nunits) break;  // uniform across the workgroup
+    const int u = base + i * nthr + (int)threadIdx.x;
+    const bool ok = u < nunits;
+    const int uu = ok ? u : 0;
+    const int t = uu & 7, g = (uu >> 3) & 3, rest = uu >> 5;
+    const int bl = rest % a.nbw, m = rest / a.nbw;
+    const _Float16 l0 = (_Float16)b.lo[i].x, l1 = (_Float16)b.lo[i].y,
+                   l2 = (_Float16)b.lo[i].z, l3 = (_Float16)b.lo[i].w;
+    const _Float16 h0 = (_Float16)b.hi[i].x, h1 = (_Float16)b.hi[i].y,
+                   h2 = (_Float16)b.hi[i].z, h3 = (_Float16)b.hi[i].w;
+    u4_t v;
+    v.x = pack_h2(l0, l2);
+    v.y = pack_h2(l1, l3);
+    v.z = pack_h2(h0, h2);
+    v.w = pack_h2(h1, h3);
+    float slo = ((float)l0 + (float)l1) + ((float)l2 + (float)l3);
+    float shi = ((float)h0 + (float)h1) + ((float)h2 + (float)h3);
+    slo += __shfl_xor(slo, 1);
+    shi += __shfl_xor(shi, 1);
+    slo += __shfl_xor(slo, 2);
+    shi += __shfl_xor(shi, 2);
+    slo += __shfl_xor(slo, 4);
+    shi += __shfl_xor(shi, 4);
+    if (ok) {
+      *reinterpret_cast<u4_t*>(a.lds_x + m * a.xs_m + bl * kLdsBlockStride +
+                               g * kLdsPairStride + 16 * t) = v;
+      if (t == 0) {
+        a.lds_s[m * a.ss_m + bl * 8 + 2 * g] = slo;
+        a.lds_s[m * a.ss_m + bl * 8 + 2 * g + 1] = shi;
+      }
+    }
+  }
+}
+
+// Batches after the first (only when a slice holds more than
+// kStageBatch units per thread).
+__device__ __forceinline__ void stage_rest(const StageArgs& a) {
+  const int nunits = a.M * a.nbw * 32;
+  const int step = (int)blockDim.x * kStageBatch;
+  for (int base = step; base < nunits; base += step) {
+    StageBatch b;
+    stage_issue(a, base, b);
+    stage_finish(a, base, b);
+  }
+}
+
+struct Quants {
+  uint32_t a[8], e[8], b[8], f[8];  // see the file comment: a,e low nibbles; b,f high
+};
+
+__device__ __forceinline__ void unpack(const u4_t& q0, const u4_t& q1, Quants& o) {
+  const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t s = d[t] >> 8;
+    o.a[t] = d[t] & 0x000F000Fu;
+    o.b[t] = d[t] & 0x00F000F0u;
+    o.e[t] = s & 0x000F000Fu;
+    o.f[t] = s & 0x00F000F0u;
+  }
+}
+
+__device__ __forceinline__ u4_t load_nt(const u4_t* p) { return __builtin_nontemporal_load(p); }
+
+// Weight stream. A wavefront reads its 16 rows in stages of kStageBlocks
+// super-blocks: the stage is 16 row segments of 576 contiguous bytes, read by
+// kStageLoads 128-bit loads per lane in which consecutive lanes take
+// consecutive 16-byte chunks (chunk q = lane + 64 i is row q / 36, chunk
+// q % 36 of that row's segment). Every load instruction thus covers about two
+// long contiguous runs instead of sixteen scattered pieces, which is what lets
+// the memory system run near its streaming rate. The chunks go through a
+// wave-private LDS buffer (row stride 37 chunks, so the compute reads below
+// hit distinct banks) from which lane (r, g) reads its block header and its
+// 32 quant bytes. While a stage is being computed the next one is in flight.
+constexpr int kStageBlocks = 4;
+constexpr int kSegChunks = 9 * kStageBlocks;          // 36 chunks of 16 B per row
+constexpr int kStageLoads = 16 * kSegChunks / 64;     // 9 loads per lane
+constexpr int kBufRowStride = 16 * (kSegChunks + 1);  // 592 B
+
+struct StageRegs {
+  u4_t v[kStageLoads];
+};
+
+// Per-lane constants of the stage loads: byte offset of chunk i inside the
+// wave's slice (row and position) and its LDS address.
+struct StageLane {
+  uint32_t goff[kStageLoads];  // (row * nb + blk) * 144 + part * 16, stage 0
+  uint32_t loff[kStageLoads];  // LDS byte offset from the dynamic LDS base
+  int blk[kStageLoads];        // super-block of the chunk within a stage
+};
+
+__device__ __forceinline__ void stage_lane(int lane, int nb, int n0, int N, uint32_t wbuf,
+                                           StageLane& c) {
+#pragma unroll
+  for (int i = 0; i < kStageLoads; ++i) {
+    const int q = lane + 64 * i;
+    const int row = q / kSegChunks, cc = q % kSegChunks;
+    const int rr = min(n0 + row, N - 1) - n0;  // rows past N re-read row N-1
+    c.blk[i] = cc / 9;
+    c.goff[i] = (uint32_t)((rr * nb + cc / 9) * kBlockBytes + (cc % 9) * 16);
+    c.loff[i] = wbuf + (uint32_t)(row * kBufRowStride + cc * 16);
+  }
+}
+
+// Issue the loads of stage s (super-blocks 4s .. 4s+3 of the slice). A full
+// stage is a wave-uniform base plus each lane's 32-bit offsets (no vector
+// address arithmetic); in a partial last stage, chunks past the slice end
+// re-read the slice's last block and are never used.
+__device__ __forceinline__ void stage_load(const uint8_t* wave_base, const StageLane& c, int s,
+                                           int nbw, StageRegs& sr) {
+  const uint8_t* sbase = wave_base + (size_t)s * (kStageBlocks * kBlockBytes);
+  if ((s + 1) * kStageBlocks <= nbw) {
+#pragma unroll
+    for (int i = 0; i < kStageLoads; ++i)
+      sr.v[i] = load_nt(reinterpret_cast<const u4_t*>(sbase + c.goff[i]));
+  } else {
+    const int last = nbw - 1 - s * kStageBlocks;  // last valid block of this stage
+#pragma unroll
+    for (int i = 0; i < kStageLoads; ++i) {
+      const uint32_t back = c.blk[i] > last ? (uint32_t)((c.blk[i] - last) * kBlockBytes) : 0u;
+      sr.v[i] = load_nt(reinterpret_cast<const u4_t*>(sbase + (c.goff[i] - back)));
+    }
+  }
+}
+
+__device__ __forceinline__ void stage_store(char* lds, const StageLane& c, const StageRegs& sr) {
+#pragma unroll
+  for (int i = 0; i < kStageLoads; ++i) *reinterpret_cast<u4_t*>(lds + c.loff[i]) = sr.v[i];
+}
+
+// One super-block as lane (r, g) needs it: the header and its j-pair's quants.
+struct BlockRegs {
+  u4_t hd, qa, qb;
+};
+
+__device__ __forceinline__ void read_block(const char* rowbuf, int g, int j, BlockRegs& b) {
+  const char* base = rowbuf + 9 * j * 16;
+  b.hd = *reinterpret_cast<const u4_t*>(base);
+  b.qa = *reinterpret_cast<const u4_t*>(base + 16 + 32 * g);
+  b.qb = *reinterpret_cast<const u4_t*>(base + 32 + 32 * g);
+}
+
+// Split-K. Partials are agent-scope atomic stores (performed at the device's
+// coherence point); once they are complete (s_waitcnt) one relaxed atomic add
+// on the tile's counter announces them. The wave that sees splits-1 reads the
+// other slices with agent-scope atomic loads, sums all slices in slice order,
+// and resets the counter. No L2 write-back or invalidate is needed because
+// every access to the partials is an agent-scope atomic.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool arrive_last(unsigned* counter, int splits, int lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  unsigned old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (old != (unsigned)(splits - 1)) return false;
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Sum of all slices of one output in slice order; the caller's own slice comes
+// from its register (bitwise the value it stored).
+__device__ __forceinline__ float sum_slices(const float* ws, size_t mn, int splits, int own,
+                                            float own_v, size_t idx) {
+  float v = own == 0 ? own_v : load_partial(ws + idx);
+  for (int k = 1; k < splits; ++k) v += (k == own) ? own_v : load_partial(ws + (size_t)k * mn + idx);
+  return v;
+}
+
+// ---------------------------------------------------------------- row-vector
+template <int M>
+__device__ __forceinline__ void vector_block(const BlockRegs& br, const HeaderLane& hl, const char* xg,
+                                             const float* sg, int bl, int xs_m, int ss_m,
+                                             float (&acc)[M]) {
+  const Header h = decode_header(br.hd, hl);
+  const float ca = h.d * (float)h.sc_a * 16777216.0f;  // 2^24: undo the low-nibble scale
+  const float cb = h.d * (float)h.sc_b * 1048576.0f;   // 2^20: undo the high-nibble scale
+  const float ma = -h.dmin * (float)h.m_a;
+  const float mb = -h.dmin * (float)h.m_b;
+  Quants q;
+  unpack(br.qa, br.qb, q);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const u4_t* xp = reinterpret_cast<const u4_t*>(xg + m * xs_m + bl * kLdsBlockStride);
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u4_t xv = xp[t];
+      pa = dot2(q.a[t], xv.x, pa);
+      pa = dot2(q.e[t], xv.y, pa);
+      pb = dot2(q.b[t], xv.z, pb);
+      pb = dot2(q.f[t], xv.w, pb);
+    }
+    const float2 s = *reinterpret_cast<const float2*>(sg + m * ss_m + bl * 8);
+    float v = acc[m];
+    v = fmaf(ca, pa, v);
+    v = fmaf(cb, pb, v);
+    v = fmaf(ma, s.x, v);
+    v = fmaf(mb, s.y, v);
+    acc[m] = v;
+  }
+}
+
+template <int M>
+__global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict__ x,
+                                                         const uint8_t* __restrict__ W,
+                                                         float* __restrict__ y,
+                                                         float* __restrict__ ws,
+                                                         unsigned* __restrict__ counters, int N,
+                                                         int K, int nbs, int xs_m, int ss_m) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nb = K / kBlockWeights;
+  const int slice = (int)blockIdx.y;
+  const int kb0 = slice * nbs;
+  const int nbw = min(nbs, nb - kb0);
+  const int waves = (int)blockDim.x >> 6;
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int ntiles = (N + 15) >> 4;
+  const int tile = (int)blockIdx.x * waves + wave;
+  const int n0 = min(tile, ntiles - 1) * 16;
+  const int n = tile * 16 + r;
+  const uint8_t* wave_base = W + ((size_t)n0 * nb + kb0) * kBlockBytes;
+
+  char* lds_x = lds;
+  float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
+  const uint32_t wbuf = (uint32_t)(M * xs_m + M * ss_m * 4 + wave * 16 * kBufRowStride);
+  StageLane sl;
+  stage_lane(lane, nb, n0, N, wbuf, sl);
+  const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
+  StageBatch sb;
+  stage_issue(st, 0, sb);
+  StageRegs sr;
+  stage_load(wave_base, sl, 0, nbw, sr);
+  stage_finish(st, 0, sb);
+  stage_rest(st);
+  __syncthreads();
+  if (tile >= ntiles) return;
+
+  const HeaderLane hl = header_lane(g);
+  const char* xg = lds_x + g * kLdsPairStride;
+  const float* sg = lds_s + 2 * g;
+  const char* rowbuf = lds + wbuf + r * kBufRowStride;
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
+  for (int s = 0; s < nstages; ++s) {
+    stage_store(lds, sl, sr);
+    if (s + 1 < nstages) stage_load(wave_base, sl, s + 1, nbw, sr);
+#pragma unroll
+    for (int j = 0; j < kStageBlocks; ++j) {
+      const int bl = s * kStageBlocks + j;
+      if (bl < nbw) {
+        BlockRegs br;
+        read_block(rowbuf, g, j, br);
+        vector_block<M>(br, hl, xg, sg, bl, xs_m, ss_m, acc);
+      }
+    }
+  }
+  // the four lanes of a row (g = 0..3) hold its four j-pair partials
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float v = acc[m];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    acc[m] = v;
+  }
+  const int splits = (int)gridDim.y;
+  if (splits == 1) {
+    if (n < N) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if ((m & 3) == g) y[(size_t)m * N + n] = acc[m];
+    }
+    return;
+  }
+  const size_t mn = (size_t)M * (size_t)N;
+  if (n < N) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if ((m & 3) == g) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, acc[m]);
+  }
+  if (arrive_last(counters + tile, splits, lane) && n < N) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if ((m & 3) == g)
+        y[(size_t)m * N + n] = sum_slices(ws, mn, splits, slice, acc[m], (size_t)m * N + n);
+  }
+}
+
+// --------------------------------------------------------------------- tiled
+template <int MT>
+__device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLane& hl, const char* const (&xa)[MT],
+                                            const float* const (&sa)[MT], int bl,
+                                            f4_t (&acc)[MT]) {
+  const Header h = decode_header(br.hd, hl);
+  const _Float16 sa16 = (_Float16)(float)(h.sc_a * 1024u);  // q*2^-24 -> q*sc*2^-14
+  const _Float16 sb16 = (_Float16)(float)(h.sc_b * 64u);    // q*2^-20 -> q*sc*2^-14
+  const h2_t sca = {sa16, sa16}, scb = {sb16, sb16};
+  const float dd = h.d * 16384.0f;  // 2^14
+  const float ma = -h.dmin * (float)h.m_a;
+  const float mb = -h.dmin * (float)h.m_b;
+  Quants q;
+  unpack(br.qa, br.qb, q);
+  h8_t bw[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u4_t v;
+    v.x = pk_mul(q.a[t], sca);
+    v.y = pk_mul(q.e[t], sca);
+    v.z = pk_mul(q.b[t], scb);
+    v.w = pk_mul(q.f[t], scb);
+    bw[t] = __builtin_bit_cast(h8_t, v);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const u4_t* xp = reinterpret_cast<const u4_t*>(xa[mt] + bl * kLdsBlockStride);
+    f4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xp[t]), bw[t], c, 0, 0,
+                                                 0);
+    f4_t a = acc[mt];
+    a[0] = fmaf(dd, c[0], a[0]);
+    a[1] = fmaf(dd, c[1], a[1]);
+    a[2] = fmaf(dd, c[2], a[2]);
+    a[3] = fmaf(dd, c[3], a[3]);
+    const float2 s = *reinterpret_cast<const float2*>(sa[mt] + bl * 8);
+    a = __builtin_amdgcn_mfma_f32_16x16x4f32(s.x, ma, a, 0, 0, 0);
+    a = __builtin_amdgcn_mfma_f32_16x16x4f32(s.y, mb, a, 0, 0, 0);
+    acc[mt] = a;
+  }
+}
+
+template <int MT>
+__global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict__ x,
+                                                        const uint8_t* __restrict__ W,
+                                                        float* __restrict__ y,
+                                                        float* __restrict__ ws,
+                                                        unsigned* __restrict__ counters, int M,
+                                                        int N, int K, int nbs, int xs_m,
+                                                        int ss_m) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nb = K / kBlockWeights;
+  const int slice = (int)blockIdx.y;
+  const int kb0 = slice * nbs;
+  const int nbw = min(nbs, nb - kb0);
+  const int waves = (int)blockDim.x >> 6;
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int ntiles = (N + 15) >> 4;
+  const int tile = (int)blockIdx.x * waves + wave;
+  const int n0 = min(tile, ntiles - 1) * 16;
+  const int n = tile * 16 + r;
+  const uint8_t* wave_base = W + ((size_t)n0 * nb + kb0) * kBlockBytes;
+
+  char* lds_x = lds;
+  float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
+  const uint32_t wbuf = (uint32_t)(M * xs_m + M * ss_m * 4 + wave * 16 * kBufRowStride);
+  StageLane sl;
+  stage_lane(lane, nb, n0, N, wbuf, sl);
+  const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
+  StageBatch sb;
+  stage_issue(st, 0, sb);
+  StageRegs sr;
+  stage_load(wave_base, sl, 0, nbw, sr);
+  stage_finish(st, 0, sb);
+  stage_rest(st);
+  __syncthreads();
+  if (tile >= ntiles) return;
+
+  const HeaderLane hl = header_lane(g);
+  // A-operand rows this lane reads (rows past M repeat row M-1; their outputs
+  // are never stored, and an MFMA output row depends on its A row only)
+  const char* xa[MT];
+  const float* sa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int mr = min(16 * mt + r, M - 1);
+    xa[mt] = lds_x + mr * xs_m + g * kLdsPairStride;
+    sa[mt] = lds_s + mr * ss_m + 2 * g;
+  }
+  const char* rowbuf = lds + wbuf + r * kBufRowStride;
+  f4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
+  for (int s = 0; s < nstages; ++s) {
+    stage_store(lds, sl, sr);
+    if (s + 1 < nstages) stage_load(wave_base, sl, s + 1, nbw, sr);
+#pragma unroll
+    for (int j = 0; j < kStageBlocks; ++j) {
+      const int bl = s * kStageBlocks + j;
+      if (bl < nbw) {
+        BlockRegs br;
+        read_block(rowbuf, g, j, br);
+        tiled_block<MT>(br, hl, xa, sa, bl, acc);
+      }
+    }
+  }
+  const int splits = (int)gridDim.y;
+  if (splits == 1) {
+    if (n < N) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * mt + 4 * g + i;
+          if (m < M) y[(size_t)m * N + n] = acc[mt][i];
+        }
+    }
+    return;
+  }
+  const size_t mn = (size_t)M * (size_t)N;
+  if (n < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * g + i;
+        if (m < M) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, acc[mt][i]);
+      }
+  }
+  if (arrive_last(counters + tile, splits, lane) && n < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * g + i;
+        if (m < M)
+          y[(size_t)m * N + n] = sum_slices(ws, mn, splits, slice, acc[mt][i], (size_t)m * N + n);
+      }
+  }
+}
+
+template <int M>
+hipError_t launch_vector(const Launch& a, hipStream_t stream) {
+  dim3 grid(a.grid_x, a.splits), block(64 * a.waves_per_wg);
+  hipLaunchKernelGGL(qmm_vector_kernel<M>, grid, block, a.lds_bytes, stream, a.x,
+                     static_cast<const uint8_t*>(a.W), a.y, a.ws, a.counters, a.N, a.K, a.nbs,
+                     a.xs_m, a.ss_m);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_tiled(const Launch& a, hipStream_t stream) {
+  dim3 grid(a.grid_x, a.splits), block(64 * a.waves_per_wg);
+  hipLaunchKernelGGL(qmm_tiled_kernel<MT>, grid, block, a.lds_bytes, stream, a.x,
+                     static_cast<const uint8_t*>(a.W), a.y, a.ws, a.counters, a.M, a.N, a.K,
+                     a.nbs, a.xs_m, a.ss_m);
+  return hipGetLastError();
+}
+
+typedef hipError_t (*LaunchFn)(const Launch&, hipStream_t);
+
+constexpr LaunchFn kVector[32] = {
+    launch_vector<1>,  launch_vector<2>,  launch_vector<3>,  launch_vector<4>,
+    launch_vector<5>,  launch_vector<6>,  launch_vector<7>,  launch_vector<8>,
+    launch_vector<9>,  launch_vector<10>, launch_vector<11>, launch_vector<12>,
+    launch_vector<13>, launch_vector<14>, launch_vector<15>, launch_vector<16>,
+    launch_vector<17>, launch_vector<18>, launch_vector<19>, launch_vector<20>,
+    launch_vector<21>, launch_vector<22>, launch_vector<23>, launch_vector<24>,
+    launch_vector<25>, launch_vector<26>, launch_vector<27>, launch_vector<28>,
+    launch_vector<29>, launch_vector<30>, launch_vector<31>, launch_vector<32>};
+
+template <int M>
+hipError_t raise_vector() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_vector_kernel<M>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+}
+constexpr hipError_t (*kRaiseVector[32])() = {
+    raise_vector<1>,  raise_vector<2>,  raise_vector<3>,  raise_vector<4>,  raise_vector<5>,
+    raise_vector<6>,  raise_vector<7>,  raise_vector<8>,  raise_vector<9>,  raise_vector<10>,
+    raise_vector<11>, raise_vector<12>, raise_vector<13>, raise_vector<14>, raise_vector<15>,
+    raise_vector<16>, raise_vector<17>, raise_vector<18>, raise_vector<19>, raise_vector<20>,
+    raise_vector<21>, raise_vector<22>, raise_vector<23>, raise_vector<24>, raise_vector<25>,
+    raise_vector<26>, raise_vector<27>, raise_vector<28>, raise_vector<29>, raise_vector<30>,
+    raise_vector<31>, raise_vector<32>};
+
+}  // namespace
+
+hipError_t prepare_kernels() {
+  for (int i = 0; i < 32; ++i) {
+    hipError_t e = kRaiseVector[i]();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_tiled_kernel<1>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_tiled_kernel<2>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+}
+
+hipError_t launch(const Launch& a, hipStream_t stream) {
+  if (a.kernel == 2) return a.M > 16 ? launch_tiled<2>(a, stream) : launch_tiled<1>(a, stream);
+  return kVector[a.M - 1](a, stream);
+}
+
+}  // namespace qmm
