@@ -69,7 +69,7 @@ int make_plan(const qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   } else {
     // fewest slices whose activations fit in LDS ...
     int s_lds = 1;
-    while (s_lds < nb && qmm::lds_bytes((int)M, (nb + s_lds - 1) / s_lds, waves) > qmm::kLdsMax) ++s_lds;
+    while (s_lds < nb && qmm::lds_bytes((int)M, (nb + s_lds - 1) / s_lds, waves, kernel) > qmm::kLdsMax) ++s_lds;
     // ... and enough row-tile work items to fill the chip, keeping at least a
     // ring's worth of super-blocks per slice
     int s_par = 1;
@@ -80,7 +80,7 @@ int make_plan(const qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   }
   const int nbs = (nb + splits - 1) / splits;
   splits = (nb + nbs - 1) / nbs;  // no empty slice
-  const int lds = qmm::lds_bytes((int)M, nbs, waves);
+  const int lds = qmm::lds_bytes((int)M, nbs, waves, kernel);
   if (lds > qmm::kLdsMax) return QMM_ERR_INVALID_ARG;
   const int64_t ws = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
   if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
@@ -256,7 +256,7 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_
   a.splits = p.splits;
   a.grid_x = p.grid_x;
   a.nbs = p.blocks_per_split;
-  a.xs_m = qmm::lds_xs_m(p.blocks_per_split);
+  a.xs_m = qmm::lds_xs_m(p.blocks_per_split, p.kernel);
   a.ss_m = qmm::lds_ss_m(p.blocks_per_split);
   a.lds_bytes = p.lds_bytes;
   a.x = x;

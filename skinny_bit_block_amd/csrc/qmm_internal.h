@@ -37,18 +37,25 @@ struct Launch {
 // Row tiles a split-K call may have (one arrival counter each).
 constexpr int64_t kMaxCounterTiles = 1 << 20;
 
-// Per-row LDS strides for nbw staged super-blocks.
-inline int lds_xs_m(int nbw) {
-  // a row stride congruent to 64 mod 128 spreads the 16 rows an MFMA operand
-  // read touches over all banks
+// Per-row LDS strides for nbw staged super-blocks. Tiled kernel: a row
+// stride congruent to 64 mod 128 spreads the 16 rows an MFMA operand read
+// touches over all banks. Row-vector kernel: 512 B per block, no padding (its
+// reads are lane-contiguous).
+inline int lds_xs_m(int nbw, int kernel) {
+  if (kernel == 1) return nbw * 512;
   return nbw * kLdsBlockStride + ((nbw & 1) ? 0 : 64);
 }
 inline int lds_ss_m(int nbw) { return nbw * 8 + 2; }
 // Per-wavefront transpose buffer of the weight stream: 16 rows x (4 blocks =
 // 36 chunks of 16 B + one chunk of padding).
 constexpr int kWaveBufBytes = 16 * 16 * 37;
-inline int lds_bytes(int M, int nbw, int waves) {
-  return M * lds_xs_m(nbw) + M * lds_ss_m(nbw) * 4 + waves * kWaveBufBytes;
+// The per-wave weight buffers start 16-byte aligned after the staged
+// activations and sub-block sums.
+__host__ __device__ inline int lds_wbuf_base(int M, int xs_m, int ss_m) {
+  return (M * xs_m + M * ss_m * 4 + 15) & ~15;
+}
+inline int lds_bytes(int M, int nbw, int waves, int kernel) {
+  return lds_wbuf_base(M, lds_xs_m(nbw, kernel), lds_ss_m(nbw)) + waves * kWaveBufBytes;
 }
 
 hipError_t launch(const Launch& a, hipStream_t stream);

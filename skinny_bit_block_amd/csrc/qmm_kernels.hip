@@ -171,6 +171,15 @@ __device__ __forceinline__ void stage_issue(const StageArgs& a, int base, StageB
   }
 }
 
+// Layouts of the staged activations (units of 16 B = 8 binary16 values):
+//   kUnitLayout (tiled kernel): unit (m, bl, g, t) at m*xs_m + bl*576 + g*144
+//     + 16t, dwords in the order the MFMA operand takes them;
+//   kLaneLayout (row-vector kernel): the 32 dwords d = 4t + c of (m, bl, g)
+//     at m*xs_m + bl*512 + g*128, dword d at position 2*(d % 16) + d / 16, so
+//     lane r of a 16-lane row reads dwords r and 16 + r with one 8-byte load.
+enum { kUnitLayout = 0, kLaneLayout = 1 };
+
+template <int L>
 __device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const StageBatch& b) {
   const int nunits = a.M * a.nbw * 32;
   const int nthr = (int)blockDim.x;
@@ -200,8 +209,17 @@ __device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const
     slo += __shfl_xor(slo, 4);
     shi += __shfl_xor(shi, 4);
     if (ok) {
-      *reinterpret_cast<u4_t*>(a.lds_x + m * a.xs_m + bl * kLdsBlockStride +
-                               g * kLdsPairStride + 16 * t) = v;
+      if (L == kUnitLayout) {
+        *reinterpret_cast<u4_t*>(a.lds_x + m * a.xs_m + bl * kLdsBlockStride +
+                                 g * kLdsPairStride + 16 * t) = v;
+      } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
+        const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
+        dst[p0] = v.x;
+        dst[p0 + 2] = v.y;
+        dst[p0 + 4] = v.z;
+        dst[p0 + 6] = v.w;
+      }
       if (t == 0) {
         a.lds_s[m * a.ss_m + bl * 8 + 2 * g] = slo;
         a.lds_s[m * a.ss_m + bl * 8 + 2 * g + 1] = shi;
@@ -212,13 +230,14 @@ __device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const
 
 // Batches after the first (only when a slice holds more than
 // kStageBatch units per thread).
+template <int L>
 __device__ __forceinline__ void stage_rest(const StageArgs& a) {
   const int nunits = a.M * a.nbw * 32;
   const int step = (int)blockDim.x * kStageBatch;
   for (int base = step; base < nunits; base += step) {
     StageBatch b;
     stage_issue(a, base, b);
-    stage_finish(a, base, b);
+    stage_finish<L>(a, base, b);
   }
 }
 
@@ -354,10 +373,48 @@ __device__ __forceinline__ float sum_slices(const float* ws, size_t mn, int spli
 }
 
 // ---------------------------------------------------------------- row-vector
+// Eight v_dot2c_f32_f16 whose first operand is an x dword broadcast from lane
+// n of the lane's 16-lane row (DPP row_newbcast:n): lanes of a row share their
+// j-pair, so each holds two of its 32 x dwords and the row reads them from one
+// another without touching LDS. The compiler cannot see hazards inside asm, so
+// the asm keeps two distances itself. A DPP instruction must not read a VGPR
+// that a VALU instruction wrote in the two previous slots, so every block of
+// eight starts with s_nop 1 for the operands written just before it. And the
+// tied accumulator of a DPP dot is read back later than that: on gfx950 a dot
+// that reads its accumulator four slots after the previous dot wrote it adds
+// to a stale value, so the eight dots of a block write eight different
+// accumulators, and each is read again seven dots later at the earliest.
+#define QMM_DOT(acc, w, n) "v_dot2c_f32_f16_dpp %[" acc "], %[x], %[" w "] row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
+#define QMM_DOT8(n0, n1, n2, n3, n4, n5, n6, n7)                                            \
+  "s_nop 1\n" QMM_DOT("c0", "w0", n0) QMM_DOT("c1", "w1", n1) QMM_DOT("c2", "w2", n2)        \
+      QMM_DOT("c3", "w3", n3) QMM_DOT("c4", "w4", n4) QMM_DOT("c5", "w5", n5)              \
+          QMM_DOT("c6", "w6", n6) QMM_DOT("c7", "w7", n7)
+#define QMM_DOT_OPERANDS(T)                                                                    \
+  : [c0] "+v"(p.c[0]), [c1] "+v"(p.c[1]), [c2] "+v"(p.c[2]), [c3] "+v"(p.c[3]),                \
+    [c4] "+v"(p.c[4]), [c5] "+v"(p.c[5]), [c6] "+v"(p.c[6]), [c7] "+v"(p.c[7])                 \
+  : [x] "v"(x), [w0] "v"(q.a[T]), [w1] "v"(q.e[T]), [w2] "v"(q.b[T]), [w3] "v"(q.f[T]),       \
+    [w4] "v"(q.a[T + 1]), [w5] "v"(q.e[T + 1]), [w6] "v"(q.b[T + 1]), [w7] "v"(q.f[T + 1])
+
+// c0, c1, c4, c5 sum low nibbles (sub-block 2g), c2, c3, c6, c7 high nibbles
+// (sub-block 2g+1)
+struct DotAcc {
+  float c[8];
+};
+
+// dwords d = 4t + c of the j-pair for t = T, T+1: c = 0, 1 feed P_a (low
+// nibbles, sub-block 2g), c = 2, 3 feed P_b (high nibbles, sub-block 2g+1)
+template <int T>
+__device__ __forceinline__ void dots8(DotAcc& p, uint32_t x, const Quants& q) {
+  if (T % 4 == 0)
+    asm(QMM_DOT8(0, 1, 2, 3, 4, 5, 6, 7) QMM_DOT_OPERANDS(T));
+  else
+    asm(QMM_DOT8(8, 9, 10, 11, 12, 13, 14, 15) QMM_DOT_OPERANDS(T));
+}
+
 template <int M>
-__device__ __forceinline__ void vector_block(const BlockRegs& br, const HeaderLane& hl, const char* xg,
-                                             const float* sg, int bl, int xs_m, int ss_m,
-                                             float (&acc)[M]) {
+__device__ __forceinline__ void vector_block(const BlockRegs& br, const HeaderLane& hl,
+                                             const char* xl, const float* sg, int bl, int xs_m,
+                                             int ss_m, float (&acc)[M]) {
   const Header h = decode_header(br.hd, hl);
   const float ca = h.d * (float)h.sc_a * 16777216.0f;  // 2^24: undo the low-nibble scale
   const float cb = h.d * (float)h.sc_b * 1048576.0f;   // 2^20: undo the high-nibble scale
@@ -367,16 +424,15 @@ __device__ __forceinline__ void vector_block(const BlockRegs& br, const HeaderLa
   unpack(br.qa, br.qb, q);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const u4_t* xp = reinterpret_cast<const u4_t*>(xg + m * xs_m + bl * kLdsBlockStride);
-    float pa = 0.f, pb = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u4_t xv = xp[t];
-      pa = dot2(q.a[t], xv.x, pa);
-      pa = dot2(q.e[t], xv.y, pa);
-      pb = dot2(q.b[t], xv.z, pb);
-      pb = dot2(q.f[t], xv.w, pb);
-    }
+    // this lane's two x dwords of (m, block, j-pair): d = r and d = 16 + r
+    const uint2 xv = *reinterpret_cast<const uint2*>(xl + m * xs_m + bl * 512);
+    DotAcc p{{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+    dots8<0>(p, xv.x, q);
+    dots8<2>(p, xv.x, q);
+    dots8<4>(p, xv.y, q);
+    dots8<6>(p, xv.y, q);
+    const float pa = (p.c[0] + p.c[1]) + (p.c[4] + p.c[5]);
+    const float pb = (p.c[2] + p.c[3]) + (p.c[6] + p.c[7]);
     const float2 s = *reinterpret_cast<const float2*>(sg + m * ss_m + bl * 8);
     float v = acc[m];
     v = fmaf(ca, pa, v);
@@ -410,7 +466,7 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
-  const uint32_t wbuf = (uint32_t)(M * xs_m + M * ss_m * 4 + wave * 16 * kBufRowStride);
+  const uint32_t wbuf = (uint32_t)(lds_wbuf_base(M, xs_m, ss_m) + wave * 16 * kBufRowStride);
   StageLane sl;
   stage_lane(lane, nb, n0, N, wbuf, sl);
   const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
@@ -418,13 +474,13 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
   stage_issue(st, 0, sb);
   StageRegs sr;
   stage_load(wave_base, sl, 0, nbw, sr);
-  stage_finish(st, 0, sb);
-  stage_rest(st);
+  stage_finish<kLaneLayout>(st, 0, sb);
+  stage_rest<kLaneLayout>(st);
   __syncthreads();
   if (tile >= ntiles) return;
 
   const HeaderLane hl = header_lane(g);
-  const char* xg = lds_x + g * kLdsPairStride;
+  const char* xl = lds_x + g * 128 + 8 * r;
   const float* sg = lds_s + 2 * g;
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
   float acc[M];
@@ -440,7 +496,7 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
       if (bl < nbw) {
         BlockRegs br;
         read_block(rowbuf, g, j, br);
-        vector_block<M>(br, hl, xg, sg, bl, xs_m, ss_m, acc);
+        vector_block<M>(br, hl, xl, sg, bl, xs_m, ss_m, acc);
       }
     }
   }
@@ -543,7 +599,7 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
-  const uint32_t wbuf = (uint32_t)(M * xs_m + M * ss_m * 4 + wave * 16 * kBufRowStride);
+  const uint32_t wbuf = (uint32_t)(lds_wbuf_base(M, xs_m, ss_m) + wave * 16 * kBufRowStride);
   StageLane sl;
   stage_lane(lane, nb, n0, N, wbuf, sl);
   const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
@@ -551,21 +607,24 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   stage_issue(st, 0, sb);
   StageRegs sr;
   stage_load(wave_base, sl, 0, nbw, sr);
-  stage_finish(st, 0, sb);
-  stage_rest(st);
+  stage_finish<kUnitLayout>(st, 0, sb);
+  stage_rest<kUnitLayout>(st);
   __syncthreads();
   if (tile >= ntiles) return;
 
   const HeaderLane hl = header_lane(g);
-  // A-operand rows this lane reads (rows past M repeat row M-1; their outputs
-  // are never stored, and an MFMA output row depends on its A row only)
+  // A-operand rows this lane reads. An MFMA output row depends only on its A
+  // row, and rows past M are never stored, so those lanes read arbitrary
+  // in-bounds data: staged row 0 shifted by 16 B per lane, which keeps the 16
+  // lanes of a read at distinct addresses (a shared address serializes).
   const char* xa[MT];
   const float* sa[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int mr = min(16 * mt + r, M - 1);
-    xa[mt] = lds_x + mr * xs_m + g * kLdsPairStride;
-    sa[mt] = lds_s + mr * ss_m + 2 * g;
+    const int mr = 16 * mt + r;
+    const bool real = mr < M;
+    xa[mt] = lds_x + (real ? mr * xs_m : 16 * (mr - M)) + g * kLdsPairStride;
+    sa[mt] = lds_s + (real ? mr * ss_m : 2 * (mr - M)) + 2 * g;
   }
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
   f4_t acc[MT];
