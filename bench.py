@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-eager", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="one allocation per matrix instead of one weight arena")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--layers", type=int, default=64, help="(for quick tests only; the metric needs 64)")
     return ap.parse_args()
@@ -59,7 +61,7 @@ def parse():
 class Pass:
     """Device-resident weights, activations and outputs of one full model pass."""
 
-    def __init__(self, torch, sbb, synth, acc, ms, layers):
+    def __init__(self, torch, sbb, synth, acc, ms, layers, arena=True):
         self.torch, self.sbb = torch, sbb
         self.shapes = [s for s in acc.full_pass_shapes()
                        if s[0] == "lm_head" or int(s[0][1:].split(".")[0]) < layers]
@@ -69,6 +71,14 @@ class Pass:
         self.W = []
         bufs = {}
         t0 = time.time()
+        # all matrices in one device allocation, each at a 2 MiB-aligned offset
+        # (the way an inference engine keeps its weights)
+        align = 2 << 20
+        offs, total = [], 0
+        for _, N, K in self.shapes:
+            offs.append(total)
+            total += -(-acc.weight_bytes(N, K) // align) * align
+        self.arena = torch.empty(total, dtype=torch.uint8, device=dev) if arena else None
         for i, (name, N, K) in enumerate(self.shapes):
             nbytes = acc.weight_bytes(N, K)
             if nbytes not in bufs:
@@ -76,7 +86,10 @@ class Pass:
                 bufs[nbytes] = np.empty(nbytes, dtype=np.uint8)
             host = bufs[nbytes]
             synth.weights(N, K, tensor=i + 1, seed=SEED, out=host.reshape(N, -1))
-            d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            if arena:
+                d = self.arena[offs[i]:offs[i] + nbytes]
+            else:
+                d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
             d.copy_(torch.from_numpy(host))
             self.W.append(d)
             if i % 64 == 0:
@@ -132,8 +145,8 @@ class Pass:
     def kernel_symbol(self, M, N, K):
         p = self.plan(M, N, K)
         if p["kernel"] == self.sbb.KERNEL_TILED:
-            return "qmm_tiled_kernel<%d>" % (1 if M <= 16 else 2)
-        return "qmm_vector_kernel<%d>" % M
+            return "qmm_tiled_kernel<%d, %d>" % (1 if M <= 16 else 2, p["ring"])
+        return "qmm_vector_kernel<%d, %d>" % (M, p["ring"])
 
 
 def time_passes(P, steps, warmup, graph):
@@ -252,7 +265,7 @@ def cpu_baseline(budget_s):
 
 def mode_pass(args, torch, sbb, synth, acc):
     ms = [int(v) for v in args.ms.split(",")]
-    P = Pass(torch, sbb, synth, acc, ms, args.layers)
+    P = Pass(torch, sbb, synth, acc, ms, args.layers, arena=not args.separate)
     if not args.no_graph:
         P.capture()
         log("graphs captured")
@@ -312,7 +325,7 @@ def mode_pass(args, torch, sbb, synth, acc):
 def mode_kernels(args, torch, sbb, synth, acc):
     """Only the per-launch timing region (one eager pass per M): for rocprofv3."""
     ms = [int(v) for v in args.ms.split(",")]
-    P = Pass(torch, sbb, synth, acc, ms, args.layers)
+    P = Pass(torch, sbb, synth, acc, ms, args.layers, arena=not args.separate)
     for _ in range(max(1, args.steps)):
         sym = kernel_timing(P, ms)
     print(json.dumps({s: {"launches": v["launches"], "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),

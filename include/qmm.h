@@ -116,7 +116,7 @@ uint64_t qmm_weight_bytes(int64_t N, int64_t K);
 enum {
   QMM_KERNEL_AUTO = 0,  /* let the launch table decide (for overrides) */
   QMM_KERNEL_VECTOR = 1, /* row-vector kernel: VALU dot products, x broadcast */
-  QMM_KERNEL_TILED = 2   /* tiled kernel: MFMA 16x16x32 f16, M >= 8 only */
+  QMM_KERNEL_TILED = 2   /* tiled kernel: MFMA 16x16x32 f16 (rows padded to 16) */
 };
 
 /* One launch-table entry: which kernel, how the grid is shaped. */
@@ -124,9 +124,16 @@ typedef struct {
   int32_t kernel;        /* QMM_KERNEL_VECTOR or QMM_KERNEL_TILED */
   int32_t waves_per_wg;  /* wavefronts per workgroup: 1, 2, 4 or 8 */
   int32_t splits;        /* K split into this many slices (1 = no split-K) */
-  int32_t grid_x;        /* workgroups per K slice (one 16-row tile per wavefront) */
+  int32_t grid_x;        /* workgroups per K slice; each wavefront walks the 16-row
+                            tiles b*waves + w, + grid_x*waves, ... of its slice, so
+                            the table never launches more workgroups than the
+                            device holds at once (nor more than one tile per
+                            wavefront needs) */
   int32_t blocks_per_split; /* super-blocks along K per slice */
   int32_t lds_bytes;     /* LDS per workgroup */
+  int32_t ring;          /* weight stages a wavefront keeps in registers: while it
+                            computes one stage from LDS, the loads of ring-1
+                            more are in flight (1 or 2) */
   int64_t workspace_bytes; /* split-K partials used (0 when splits == 1) */
 } qmm_plan;
 
@@ -135,19 +142,24 @@ typedef struct {
 int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out);
 
 /* Force a kernel for every following call on this handle (QMM_KERNEL_AUTO
- * restores the table). QMM_KERNEL_TILED with M < 8 makes qmm_run return
- * QMM_ERR_INVALID_ARG. For tests and sweeps. */
+ * restores the table). For tests and sweeps. */
 int qmm_set_kernel(qmm_handle h, int kernel);
 
 /* Override the grid shape for every following call: waves_per_wg (0 = table),
- * splits (0 = table), grid_x (0 = table; otherwise at least the number of
- * workgroups the call needs, one 16-row tile per wavefront). Values that do
- * not fit the call (LDS, workspace, K, grid) make qmm_run return
- * QMM_ERR_INVALID_ARG. For sweeps. */
+ * splits (0 = table), grid_x (0 = table; any positive count works: with fewer
+ * workgroups each wavefront walks more tiles, with more some stay idle).
+ * Values that do not fit the call (LDS, workspace, K) make qmm_run return
+ * QMM_ERR_INVALID_ARG. On a planning-only handle the table's grid_x is one
+ * tile per wavefront (the device's capacity is unknown there). For sweeps. */
 int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x);
 
+/* Override the register stages of the weight stream for every following
+ * call (0 = table, else 1 or 2; other values return QMM_ERR_INVALID_ARG).
+ * For sweeps. */
+int qmm_set_ring(qmm_handle h, int ring);
+
 /* The row count from which the launch table switches from the row-vector to
- * the tiled kernel (M >= switch uses the tiled kernel; never below 8). */
+ * the tiled kernel (M >= switch uses the tiled kernel). */
 int qmm_switch_point(qmm_handle h, int64_t N, int64_t K);
 
 #ifdef __cplusplus

@@ -17,11 +17,18 @@
 #include "../../include/qmm.h"
 #include "qmm_internal.h"
 
+// Cached occupancy query: workgroups per compute unit for one launch shape.
+struct qmm_occ {
+  int kernel, M, ring, waves, lds, wgs;
+};
+
 struct qmm_ctx {
   int device;           // -1: planning-only handle (no device, no workspace)
   int cus;              // compute units
+  qmm_occ occ[64];      // small cache of occupancy queries (launch shapes seen)
+  int nocc;
   int forced_kernel;    // QMM_KERNEL_*
-  int force_waves, force_splits, force_grid;
+  int force_waves, force_splits, force_grid, force_ring;
   float* ws;            // split-K partials
   int64_t ws_bytes;
   unsigned* counters;   // split-K arrival counters, one per row tile, zeroed at creation
@@ -32,9 +39,10 @@ namespace {
 constexpr int64_t kWorkspaceBytes = 128ll << 20;
 constexpr int kGfx950Cus = 256;
 constexpr int kDefaultWaves = 4;
+constexpr int kDefaultRing = 1;
 // Split K until there are at least this many row tiles of work (a wave per
 // tile); below that the chip cannot keep enough loads in flight.
-constexpr int64_t kTargetTiles = 2048;
+constexpr int64_t kTargetTiles = 1024;
 constexpr int kMinBlocksPerSlice = 4;
 
 int check_shape(int64_t M, int64_t N, int64_t K) {
@@ -44,22 +52,85 @@ int check_shape(int64_t M, int64_t N, int64_t K) {
   return QMM_OK;
 }
 
-int table_switch(int64_t N, int64_t K) {
-  (void)N;
-  (void)K;
-  return 8;
+// Measured entries of the launch table (gfx950, MI355X): the fastest
+// (kernel, waves per workgroup, K slices) of a sweep over those three, timed
+// on the distinct matrices of a model pass in sequence (cold weights), per
+// matrix shape of the pass and per range of rows; rows between measured
+// points take the entry below them.
+struct TableEntry {
+  int32_t N, K, m_lo, kernel, waves, splits;
+};
+constexpr TableEntry kTable[] = {
+    // 5120 x 5120 projections
+    {5120, 5120, 1, QMM_KERNEL_VECTOR, 4, 5},
+    {5120, 5120, 2, QMM_KERNEL_TILED, 4, 3},
+    // gate+up, N = 2 x 17408
+    {34816, 5120, 1, QMM_KERNEL_VECTOR, 4, 1},
+    {34816, 5120, 2, QMM_KERNEL_TILED, 4, 1},
+    {34816, 5120, 16, QMM_KERNEL_TILED, 8, 2},
+    // down
+    {5120, 17408, 1, QMM_KERNEL_VECTOR, 4, 5},
+    {5120, 17408, 2, QMM_KERNEL_TILED, 4, 3},
+    {5120, 17408, 16, QMM_KERNEL_TILED, 4, 5},
+    // lm_head
+    {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1},
+    {151936, 5120, 2, QMM_KERNEL_TILED, 4, 1},
+    {151936, 5120, 16, QMM_KERNEL_TILED, 8, 2},
+};
+
+// The entry for (M, N, K), or nullptr when the shape is not in the table.
+const TableEntry* table_entry(int64_t M, int64_t N, int64_t K) {
+  const TableEntry* best = nullptr;
+  for (const TableEntry& e : kTable)
+    if (e.N == N && e.K == K && e.m_lo <= M && (!best || e.m_lo > best->m_lo)) best = &e;
+  return best;
 }
 
-int make_plan(const qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
+// Shapes outside the table: the row-vector kernel for one row, the tiled
+// kernel from two rows on (where the sweeps put the switch for every shape).
+int table_switch(int64_t N, int64_t K) {
+  const TableEntry* e1 = table_entry(1, N, K);
+  if (e1 && e1->kernel == QMM_KERNEL_TILED) return 1;
+  return 2;
+}
+
+// Workgroups of one launch shape the whole device holds at once; 0 when
+// unknown (planning-only handle, or the query failed).
+int64_t resident(qmm_ctx* h, int kernel, int M, int ring, int waves, int lds) {
+  if (h->device < 0) return 0;
+  for (int i = 0; i < h->nocc; ++i) {
+    const qmm_occ& o = h->occ[i];
+    if (o.kernel == kernel && o.M == M && o.ring == ring && o.waves == waves && o.lds == lds)
+      return (int64_t)o.wgs * h->cus;
+  }
+  int prev = 0, wgs = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return 0;
+  const bool sw = prev != h->device;
+  if (sw && hipSetDevice(h->device) != hipSuccess) return 0;
+  const hipError_t e = qmm::resident_per_cu(kernel, M, ring, waves, lds, &wgs);
+  if (sw) (void)hipSetDevice(prev);
+  if (e != hipSuccess || wgs < 1) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int slot = h->nocc < 64 ? h->nocc++ : (int)((uint32_t)(kernel * 131 + M * 31 + waves * 7 + lds) % 64u);
+  h->occ[slot] = qmm_occ{kernel, M, ring, waves, lds, wgs};
+  return (int64_t)wgs * h->cus;
+}
+
+int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   int rc = check_shape(M, N, K);
   if (rc) return rc;
   const int nb = (int)(K / 256);
   const int64_t ntiles = (N + 15) / 16;
+  const TableEntry* te = table_entry(M, N, K);
   int kernel = M >= table_switch(N, K) ? QMM_KERNEL_TILED : QMM_KERNEL_VECTOR;
+  if (te) kernel = te->kernel;
   if (h->forced_kernel != QMM_KERNEL_AUTO) kernel = h->forced_kernel;
-  if (kernel == QMM_KERNEL_TILED && M < 8) return QMM_ERR_INVALID_ARG;
 
-  const int waves = h->force_waves ? h->force_waves : kDefaultWaves;
+  const int waves = h->force_waves ? h->force_waves
+                                   : (te ? te->waves : (ntiles >= 4096 ? 8 : kDefaultWaves));
+  const int ring = h->force_ring ? h->force_ring : kDefaultRing;
   if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return QMM_ERR_INVALID_ARG;
 
   int splits;
@@ -73,9 +144,13 @@ int make_plan(const qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
     // ... and enough row-tile work items to fill the chip, keeping at least a
     // ring's worth of super-blocks per slice
     int s_par = 1;
-    while (ntiles * s_par < kTargetTiles && (nb + s_par) / (s_par + 1) >= kMinBlocksPerSlice &&
-           ntiles <= qmm::kMaxCounterTiles)
-      ++s_par;
+    if (te) {
+      s_par = te->splits < nb ? te->splits : nb;
+    } else {
+      while (ntiles * s_par < kTargetTiles && (nb + s_par) / (s_par + 1) >= kMinBlocksPerSlice &&
+             ntiles <= qmm::kMaxCounterTiles)
+        ++s_par;
+    }
     splits = s_lds > s_par ? s_lds : s_par;
   }
   const int nbs = (nb + splits - 1) / splits;
@@ -86,19 +161,23 @@ int make_plan(const qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
   if (splits > 1 && ntiles > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
 
-  // one row tile per wavefront
+  // at most one row tile per wavefront, and no more workgroups than the device
+  // holds at once: the waves then walk several tiles each (persistent grid)
   const int64_t need = (ntiles + waves - 1) / waves;
   int64_t grid = need;
-  if (h->force_grid) {
-    if (h->force_grid < need) return QMM_ERR_INVALID_ARG;
-    grid = h->force_grid;
+  const int64_t res = resident(h, kernel, (int)M, ring, waves, lds);
+  if (res > 0) {
+    const int64_t per_slice = res / splits > 0 ? res / splits : 1;
+    if (per_slice < grid) grid = per_slice;
   }
+  if (h->force_grid) grid = h->force_grid;
   if (grid > 0x7FFFFFFF) return QMM_ERR_INVALID_ARG;
 
   p->kernel = kernel;
   p->waves_per_wg = waves;
   p->splits = splits;
   p->grid_x = (int32_t)grid;
+  p->ring = ring;
   p->blocks_per_split = nbs;
   p->lds_bytes = lds;
   p->workspace_bytes = ws;
@@ -144,6 +223,7 @@ int qmm_create(qmm_handle* out, int device) {
   h->ws = nullptr;
   h->ws_bytes = kWorkspaceBytes;
   h->counters = nullptr;
+  h->nocc = 0;
   if (device == -1) {  // planning-only handle
     *out = h;
     return QMM_OK;
@@ -226,6 +306,12 @@ int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x) {
   return QMM_OK;
 }
 
+int qmm_set_ring(qmm_handle h, int ring) {
+  if (!h || ring < 0 || ring > qmm::kMaxRing) return QMM_ERR_INVALID_ARG;
+  h->force_ring = ring;
+  return QMM_OK;
+}
+
 int qmm_switch_point(qmm_handle h, int64_t N, int64_t K) {
   if (!h) return QMM_ERR_INVALID_ARG;
   return table_switch(N, K);
@@ -255,9 +341,10 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_
   a.waves_per_wg = p.waves_per_wg;
   a.splits = p.splits;
   a.grid_x = p.grid_x;
+  a.ring = p.ring;
   a.nbs = p.blocks_per_split;
   a.xs_m = qmm::lds_xs_m(p.blocks_per_split, p.kernel);
-  a.ss_m = qmm::lds_ss_m(p.blocks_per_split);
+  a.ss_m = qmm::lds_ss_m(p.blocks_per_split, p.kernel);
   a.lds_bytes = p.lds_bytes;
   a.x = x;
   a.W = W_blocks;

@@ -8,14 +8,12 @@ namespace qmm {
 
 constexpr int kBlockWeights = 256;  // weights per super-block (along K)
 constexpr int kBlockBytes = 144;    // bytes per super-block
-// LDS layout of the staged activations: one 16-byte unit per
-// (row m, super-block, j-pair g, dword t); a j-pair (two 32-weight
-// sub-blocks) is 8 units plus 16 bytes of padding, so the four j-pairs of a
-// block sit in different LDS banks.
-constexpr int kLdsPairStride = 144;
-constexpr int kLdsBlockStride = 4 * kLdsPairStride;
+// LDS layout of the staged activations: one 16-byte unit (8 binary16 values)
+// per (row m, super-block, j-pair g, dword group t); the kernels differ in
+// where a unit goes (see the kernel file).
 constexpr int kLdsMax = 160 * 1024;  // LDS a workgroup may allocate on gfx950
 constexpr int kMaxWavesPerWg = 8;
+constexpr int kMaxRing = 2;  // register stages of the weight stream a kernel may keep
 
 struct Launch {
   int kernel;       // 1 = row-vector, 2 = tiled (MFMA)
@@ -23,6 +21,7 @@ struct Launch {
   int waves_per_wg;
   int splits;       // K slices (grid.y)
   int grid_x;       // workgroups per slice
+  int ring;         // register stages of the weight stream (1..kMaxRing)
   int nbs;          // super-blocks per slice
   int xs_m;         // LDS bytes per staged activation row
   int ss_m;         // floats per row of staged sub-block sums
@@ -37,15 +36,13 @@ struct Launch {
 // Row tiles a split-K call may have (one arrival counter each).
 constexpr int64_t kMaxCounterTiles = 1 << 20;
 
-// Per-row LDS strides for nbw staged super-blocks. Tiled kernel: a row
-// stride congruent to 64 mod 128 spreads the 16 rows an MFMA operand read
-// touches over all banks. Row-vector kernel: 512 B per block, no padding (its
-// reads are lane-contiguous).
+// LDS bytes per staged activation row (nbw super-blocks: 32 units each) and
+// floats per row of sub-block sums; both kernels store them without padding.
 inline int lds_xs_m(int nbw, int kernel) {
-  if (kernel == 1) return nbw * 512;
-  return nbw * kLdsBlockStride + ((nbw & 1) ? 0 : 64);
+  (void)kernel;
+  return nbw * 512;
 }
-inline int lds_ss_m(int nbw) { return nbw * 8 + 2; }
+inline int lds_ss_m(int nbw, int kernel) { return kernel == 1 ? nbw * 8 + 2 : nbw * 8; }
 // Per-wavefront transpose buffer of the weight stream: 16 rows x (4 blocks =
 // 36 chunks of 16 B + one chunk of padding).
 constexpr int kWaveBufBytes = 16 * 16 * 37;
@@ -55,10 +52,14 @@ __host__ __device__ inline int lds_wbuf_base(int M, int xs_m, int ss_m) {
   return (M * xs_m + M * ss_m * 4 + 15) & ~15;
 }
 inline int lds_bytes(int M, int nbw, int waves, int kernel) {
-  return lds_wbuf_base(M, lds_xs_m(nbw, kernel), lds_ss_m(nbw)) + waves * kWaveBufBytes;
+  return lds_wbuf_base(M, lds_xs_m(nbw, kernel), lds_ss_m(nbw, kernel)) + waves * kWaveBufBytes;
 }
 
 hipError_t launch(const Launch& a, hipStream_t stream);
 hipError_t prepare_kernels();  // raise the dynamic-LDS limit of every kernel
+// Workgroups of the kernel a launch with these parameters uses that one
+// compute unit holds at once (registers, LDS and wave slots), on the current
+// device.
+hipError_t resident_per_cu(int kernel, int M, int ring, int waves, int lds_bytes, int* out);
 
 }  // namespace qmm

@@ -37,7 +37,8 @@
 // partials in slice order and writes y, then resets the counter for the next
 // call; which wave is last does not change the order of the sum, so results
 // are bit-identical from run to run for a given launch plan, and a call is a
-// single kernel launch. Every wave owns exactly one row tile of one K slice.
+// single kernel launch. Each wave walks a fixed sequence of row tiles of one K
+// slice (persistent workgroups).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -172,14 +173,14 @@ __device__ __forceinline__ void stage_issue(const StageArgs& a, int base, StageB
 }
 
 // Layouts of the staged activations (units of 16 B = 8 binary16 values):
-//   kUnitLayout (tiled kernel): unit (m, bl, g, t) at m*xs_m + bl*576 + g*144
-//     + 16t, dwords in the order the MFMA operand takes them;
-//   kLaneLayout (row-vector kernel): the 32 dwords d = 4t + c of (m, bl, g)
-//     at m*xs_m + bl*512 + g*128, dword d at position 2*(d % 16) + d / 16, so
-//     lane r of a 16-lane row reads dwords r and 16 + r with one 8-byte load.
-enum { kUnitLayout = 0, kLaneLayout = 1 };
-
-template <int L>
+//   row-vector kernel (stage_finish / stage_rest below): the 32 dwords
+//     d = 4t + c of (m, bl, g) at m*xs_m + bl*512 + g*128, dword d at position
+//     2*(d % 16) + d / 16, so lane r of a 16-lane row reads dwords r and 16 + r
+//     with one 8-byte load; sums[m][bl][j] at m*ss_m + bl*8 + j;
+//   tiled kernel (tstage_* further down): unit (m, bl, g, t) at
+//     16*(((bl*8 + t)*4 + g)*M + m), the order the MFMA A operand reads, so
+//     the 16 lanes of a j-pair read M consecutive units (rows past M repeat
+//     real rows); sums of (m, bl, g) as a float2 at 8*((bl*4 + g)*M + m).
 __device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const StageBatch& b) {
   const int nunits = a.M * a.nbw * 32;
   const int nthr = (int)blockDim.x;
@@ -209,17 +210,12 @@ __device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const
     slo += __shfl_xor(slo, 4);
     shi += __shfl_xor(shi, 4);
     if (ok) {
-      if (L == kUnitLayout) {
-        *reinterpret_cast<u4_t*>(a.lds_x + m * a.xs_m + bl * kLdsBlockStride +
-                                 g * kLdsPairStride + 16 * t) = v;
-      } else {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
-        const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
-        dst[p0] = v.x;
-        dst[p0 + 2] = v.y;
-        dst[p0 + 4] = v.z;
-        dst[p0 + 6] = v.w;
-      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
+      const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
+      dst[p0] = v.x;
+      dst[p0 + 2] = v.y;
+      dst[p0 + 4] = v.z;
+      dst[p0 + 6] = v.w;
       if (t == 0) {
         a.lds_s[m * a.ss_m + bl * 8 + 2 * g] = slo;
         a.lds_s[m * a.ss_m + bl * 8 + 2 * g + 1] = shi;
@@ -230,14 +226,13 @@ __device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const
 
 // Batches after the first (only when a slice holds more than
 // kStageBatch units per thread).
-template <int L>
 __device__ __forceinline__ void stage_rest(const StageArgs& a) {
   const int nunits = a.M * a.nbw * 32;
   const int step = (int)blockDim.x * kStageBatch;
   for (int base = step; base < nunits; base += step) {
     StageBatch b;
     stage_issue(a, base, b);
-    stage_finish<L>(a, base, b);
+    stage_finish(a, base, b);
   }
 }
 
@@ -279,22 +274,24 @@ struct StageRegs {
 };
 
 // Per-lane constants of the stage loads: byte offset of chunk i inside the
-// wave's slice (row and position) and its LDS address.
+// wave's slice (row and position) and its LDS address. Row tiles differ only
+// in their base address, except a last tile with fewer than 16 rows, whose
+// missing rows re-read its last row (those lanes are never stored).
 struct StageLane {
-  uint32_t goff[kStageLoads];  // (row * nb + blk) * 144 + part * 16, stage 0
+  uint32_t goff[kStageLoads];  // row * (nb * 144) + chunk * 16, stage 0
   uint32_t loff[kStageLoads];  // LDS byte offset from the dynamic LDS base
   int blk[kStageLoads];        // super-block of the chunk within a stage
 };
 
-__device__ __forceinline__ void stage_lane(int lane, int nb, int n0, int N, uint32_t wbuf,
+__device__ __forceinline__ void stage_lane(int lane, int nb, int rows, uint32_t wbuf,
                                            StageLane& c) {
 #pragma unroll
   for (int i = 0; i < kStageLoads; ++i) {
     const int q = lane + 64 * i;
     const int row = q / kSegChunks, cc = q % kSegChunks;
-    const int rr = min(n0 + row, N - 1) - n0;  // rows past N re-read row N-1
+    const int rr = min(row, rows - 1);
     c.blk[i] = cc / 9;
-    c.goff[i] = (uint32_t)((rr * nb + cc / 9) * kBlockBytes + (cc % 9) * 16);
+    c.goff[i] = (uint32_t)(rr * nb * kBlockBytes + cc * 16);  // a block is 9 chunks
     c.loff[i] = wbuf + (uint32_t)(row * kBufRowStride + cc * 16);
   }
 }
@@ -372,6 +369,39 @@ __device__ __forceinline__ float sum_slices(const float* ws, size_t mn, int spli
   return v;
 }
 
+// A wave's work is a stream of (tile, stage) elements: its tiles in order, each
+// in nstages stages of its K slice. R register stages are kept: while the
+// wave computes one element from LDS, the loads of the next R-1 are in
+// flight, across tile boundaries. Element e uses register stage e mod R; the
+// loop is unrolled by R so that the register stage is static, and the stream
+// is padded to a multiple of R. With R > 1 every step issues its loads (past
+// the end they re-read the last element), so that the wait before each use is
+// the same static count on every path; with R = 1 only real elements are
+// loaded (a wave cannot finish while loads are outstanding, so a padded load
+// would add a memory round trip to every wave's end).
+struct StreamPos {
+  int tile, s;  // next element whose loads are to be issued
+  int left;     // elements after it in the stream; -1 once it is past the end
+};
+
+template <int R>
+__device__ __forceinline__ void stream_issue(const uint8_t* slice_base, size_t row_bytes, int N,
+                                             int nb, int nbw, int nstages, int tile_step, int lane,
+                                             uint32_t wbuf, StageLane& sl, StreamPos& p,
+                                             StageRegs& dst) {
+  if (R == 1 && p.left < 0) return;
+  if (p.s == 0 && N - p.tile * 16 < 16) stage_lane(lane, nb, N - p.tile * 16, wbuf, sl);
+  stage_load(slice_base + (size_t)p.tile * 16 * row_bytes, sl, p.s, nbw, dst);
+  if (p.left > 0) {
+    if (++p.s == nstages) {
+      p.s = 0;
+      p.tile += tile_step;
+    }
+  }
+  --p.left;
+  if (R > 1 && p.left < 0) p.left = 0;
+}
+
 // ---------------------------------------------------------------- row-vector
 // Eight v_dot2c_f32_f16 whose first operand is an x dword broadcast from lane
 // n of the lane's 16-lane row (DPP row_newbcast:n): lanes of a row share their
@@ -443,7 +473,17 @@ __device__ __forceinline__ void vector_block(const BlockRegs& br, const HeaderLa
   }
 }
 
-template <int M>
+// Issue order at kernel start: every wave first issues its share of the x
+// loads, then the workgroup passes a barrier, and only then are weight loads
+// issued; so the small x reads, which every workgroup needs before it can
+// compute, are not queued behind a whole stage of weight streams.
+__device__ __forceinline__ void issue_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// The workgroups of a K slice share its row tiles round-robin: wave w of
+// workgroup b takes tiles b*waves + w, then + gridDim.x*waves, and so on, so a
+// grid no larger than what the chip holds at once stages x once per
+// workgroup.
+template <int M, int R>
 __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict__ x,
                                                          const uint8_t* __restrict__ W,
                                                          float* __restrict__ y,
@@ -456,85 +496,202 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
   const int kb0 = slice * nbs;
   const int nbw = min(nbs, nb - kb0);
   const int waves = (int)blockDim.x >> 6;
-  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform per wave
+  const int lane = (int)threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int tile = (int)blockIdx.x * waves + wave;
-  const int n0 = min(tile, ntiles - 1) * 16;
-  const int n = tile * 16 + r;
-  const uint8_t* wave_base = W + ((size_t)n0 * nb + kb0) * kBlockBytes;
+  const int tile_step = (int)gridDim.x * waves;
+  const int first = (int)blockIdx.x * waves + wave;
+  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
+  const int total = first < ntiles ? ((ntiles - 1 - first) / tile_step + 1) * nstages : 0;
+  const size_t row_bytes = (size_t)nb * kBlockBytes;
+  const uint8_t* slice_base = W + (size_t)kb0 * kBlockBytes;
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
   const uint32_t wbuf = (uint32_t)(lds_wbuf_base(M, xs_m, ss_m) + wave * 16 * kBufRowStride);
-  StageLane sl;
-  stage_lane(lane, nb, n0, N, wbuf, sl);
   const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
   StageBatch sb;
   stage_issue(st, 0, sb);
-  StageRegs sr;
-  stage_load(wave_base, sl, 0, nbw, sr);
-  stage_finish<kLaneLayout>(st, 0, sb);
-  stage_rest<kLaneLayout>(st);
+  issue_barrier();
+  StageLane sl;
+  stage_lane(lane, nb, 16, wbuf, sl);
+  StageRegs sr[R];
+  StreamPos ld{first, 0, total - 1};
+  if (total > 0) {
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
+                   sr[u]);
+  }
+  stage_finish(st, 0, sb);
+  stage_rest(st);
   __syncthreads();
-  if (tile >= ntiles) return;
 
   const HeaderLane hl = header_lane(g);
   const char* xl = lds_x + g * 128 + 8 * r;
   const float* sg = lds_s + 2 * g;
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
+  const int splits = (int)gridDim.y;
+  const size_t mn = (size_t)M * (size_t)N;
+  int tile = first, cs = 0;
   float acc[M];
+  for (int t = 0; t < total; t += R) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.f;
-  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
-  for (int s = 0; s < nstages; ++s) {
-    stage_store(lds, sl, sr);
-    if (s + 1 < nstages) stage_load(wave_base, sl, s + 1, nbw, sr);
+    for (int u = 0; u < R; ++u) {
+      stage_store(lds, sl, sr[u]);
+      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
+                   sr[u]);
+      if (t + u < total) {
+        if (cs == 0) {
 #pragma unroll
-    for (int j = 0; j < kStageBlocks; ++j) {
-      const int bl = s * kStageBlocks + j;
-      if (bl < nbw) {
-        BlockRegs br;
-        read_block(rowbuf, g, j, br);
-        vector_block<M>(br, hl, xl, sg, bl, xs_m, ss_m, acc);
+          for (int m = 0; m < M; ++m) acc[m] = 0.f;
+        }
+// block j+1's LDS reads are issued before block j is computed (the buffer
+        // holds the whole stage; past the slice end they read unused chunks)
+        BlockRegs br[2];
+        read_block(rowbuf, g, 0, br[0]);
+#pragma unroll
+        for (int j = 0; j < kStageBlocks; ++j) {
+          const int bl = cs * kStageBlocks + j;
+          if (j + 1 < kStageBlocks) read_block(rowbuf, g, j + 1, br[(j + 1) & 1]);
+          if (bl < nbw) vector_block<M>(br[j & 1], hl, xl, sg, bl, xs_m, ss_m, acc);
+        }
+        if (++cs == nstages) {
+          // the four lanes of a row (g = 0..3) hold its four j-pair partials
+          float out[M];
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float v = acc[m];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            out[m] = v;
+          }
+          const int n = tile * 16 + r;
+          if (splits == 1) {
+            if (n < N) {
+#pragma unroll
+              for (int m = 0; m < M; ++m)
+                if ((m & 3) == g) y[(size_t)m * N + n] = out[m];
+            }
+          } else {
+            if (n < N) {
+#pragma unroll
+              for (int m = 0; m < M; ++m)
+                if ((m & 3) == g) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, out[m]);
+            }
+            if (arrive_last(counters + tile, splits, lane) && n < N) {
+#pragma unroll
+              for (int m = 0; m < M; ++m)
+                if ((m & 3) == g)
+                  y[(size_t)m * N + n] = sum_slices(ws, mn, splits, slice, out[m], (size_t)m * N + n);
+            }
+          }
+          cs = 0;
+          tile += tile_step;
+        }
       }
     }
-  }
-  // the four lanes of a row (g = 0..3) hold its four j-pair partials
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float v = acc[m];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    acc[m] = v;
-  }
-  const int splits = (int)gridDim.y;
-  if (splits == 1) {
-    if (n < N) {
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        if ((m & 3) == g) y[(size_t)m * N + n] = acc[m];
-    }
-    return;
-  }
-  const size_t mn = (size_t)M * (size_t)N;
-  if (n < N) {
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if ((m & 3) == g) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, acc[m]);
-  }
-  if (arrive_last(counters + tile, splits, lane) && n < N) {
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if ((m & 3) == g)
-        y[(size_t)m * N + n] = sum_slices(ws, mn, splits, slice, acc[m], (size_t)m * N + n);
   }
 }
 
 // --------------------------------------------------------------------- tiled
+// Staging of the tiled kernel's activations: unit u = ((bl*8 + t)*4 + g)*M + m
+// goes to LDS byte 16u, so consecutive threads write consecutive units. The
+// sub-block sums are a second pass over the staged binary16 values.
+
+// q = u / d for u < 2^24 and 1 <= d <= 32: a float estimate is within one of
+// the quotient; one correction step makes it exact.
+__device__ __forceinline__ int div_small(int u, int d, float rcp) {
+  int q = (int)((float)u * rcp);
+  const int rem = u - q * d;
+  q += rem < 0 ? -1 : (rem >= d ? 1 : 0);
+  return q;
+}
+
+struct TUnit {
+  int m, g, t, bl;
+};
+
+__device__ __forceinline__ TUnit tunit(int u, int M, float rcp) {
+  const int rest = div_small(u, M, rcp);
+  return TUnit{u - rest * M, rest & 3, (rest >> 2) & 7, rest >> 5};
+}
+
+__device__ __forceinline__ void tstage_issue(const StageArgs& a, int base, float rcp,
+                                             StageBatch& b) {
+  const int nunits = a.M * a.nbw * 32;
+  const int nthr = (int)blockDim.x;
+#pragma unroll
+  for (int i = 0; i < kStageBatch; ++i) {
+    const int u = base + i * nthr + (int)threadIdx.x;
+    const TUnit c = tunit(u < nunits ? u : 0, a.M, rcp);
+    const float* src =
+        a.x + (size_t)c.m * a.K + (size_t)(a.kb0 + c.bl) * kBlockWeights + 64 * c.g + 4 * c.t;
+    b.lo[i] = *reinterpret_cast<const float4*>(src);
+    b.hi[i] = *reinterpret_cast<const float4*>(src + 32);
+  }
+}
+
+// dwords of a unit: x at block offsets 64g + {4t, 4t+2 | 4t+1, 4t+3 |
+// 32+4t, 32+4t+2 | 32+4t+1, 32+4t+3}, the order of the B operand's nibbles
+__device__ __forceinline__ void tstage_finish(const StageArgs& a, int base, const StageBatch& b) {
+  const int nunits = a.M * a.nbw * 32;
+  const int nthr = (int)blockDim.x;
+#pragma unroll
+  for (int i = 0; i < kStageBatch; ++i) {
+    const int u = base + i * nthr + (int)threadIdx.x;
+    if (u < nunits) {
+      u4_t v;
+      v.x = pack_h2((_Float16)b.lo[i].x, (_Float16)b.lo[i].z);
+      v.y = pack_h2((_Float16)b.lo[i].y, (_Float16)b.lo[i].w);
+      v.z = pack_h2((_Float16)b.hi[i].x, (_Float16)b.hi[i].z);
+      v.w = pack_h2((_Float16)b.hi[i].y, (_Float16)b.hi[i].w);
+      *reinterpret_cast<u4_t*>(a.lds_x + 16 * u) = v;
+    }
+  }
+}
+
+// Every batch but the last: issue the next batch's loads before converting
+// the current one, so that all x loads are issued before any weight load;
+// returns the base of the last batch, whose loads are in flight in cur.
+__device__ __forceinline__ int tstage_lead(const StageArgs& a, float rcp, StageBatch& cur) {
+  const int nunits = a.M * a.nbw * 32;
+  const int step = (int)blockDim.x * kStageBatch;
+  int base = 0;
+  tstage_issue(a, 0, rcp, cur);
+  for (; base + step < nunits; base += step) {
+    StageBatch next;
+    tstage_issue(a, base + step, rcp, next);
+    tstage_finish(a, base, cur);
+    cur = next;
+  }
+  return base;
+}
+
+// Sums of the rounded x over sub-blocks 2g and 2g+1 of (m, bl): entry
+// e = (bl*4 + g)*M + m, added over t = 0..7 in order. Call after a barrier.
+__device__ __forceinline__ void tstage_sums(const StageArgs& a, float rcp) {
+  const int nent = a.M * a.nbw * 4;
+  for (int e = (int)threadIdx.x; e < nent; e += (int)blockDim.x) {
+    const int rest = div_small(e, a.M, rcp);
+    const int m = e - rest * a.M, g = rest & 3, bl = rest >> 2;
+    float slo = 0.f, shi = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u4_t v =
+          *reinterpret_cast<const u4_t*>(a.lds_x + 16 * (((bl * 8 + t) * 4 + g) * a.M + m));
+      slo += (f16_lo(v.x) + f16_hi(v.x)) + (f16_lo(v.y) + f16_hi(v.y));
+      shi += (f16_lo(v.z) + f16_hi(v.z)) + (f16_lo(v.w) + f16_hi(v.w));
+    }
+    a.lds_s[2 * e] = slo;
+    a.lds_s[2 * e + 1] = shi;
+  }
+}
+
 template <int MT>
 __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLane& hl, const char* const (&xa)[MT],
-                                            const float* const (&sa)[MT], int bl,
+                                            const float* const (&sa)[MT], int bl, int M,
                                             f4_t (&acc)[MT]) {
   const Header h = decode_header(br.hd, hl);
   const _Float16 sa16 = (_Float16)(float)(h.sc_a * 1024u);  // q*2^-24 -> q*sc*2^-14
@@ -557,25 +714,26 @@ __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLan
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const u4_t* xp = reinterpret_cast<const u4_t*>(xa[mt] + bl * kLdsBlockStride);
+    const char* xp = xa[mt] + bl * 512 * M;
     f4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xp[t]), bw[t], c, 0, 0,
-                                                 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(xp + t * 64 * M)), bw[t], c, 0,
+          0, 0);
     f4_t a = acc[mt];
     a[0] = fmaf(dd, c[0], a[0]);
     a[1] = fmaf(dd, c[1], a[1]);
     a[2] = fmaf(dd, c[2], a[2]);
     a[3] = fmaf(dd, c[3], a[3]);
-    const float2 s = *reinterpret_cast<const float2*>(sa[mt] + bl * 8);
+    const float2 s = *reinterpret_cast<const float2*>(sa[mt] + bl * 8 * M);
     a = __builtin_amdgcn_mfma_f32_16x16x4f32(s.x, ma, a, 0, 0, 0);
     a = __builtin_amdgcn_mfma_f32_16x16x4f32(s.y, mb, a, 0, 0, 0);
     acc[mt] = a;
   }
 }
 
-template <int MT>
+template <int MT, int R>
 __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict__ x,
                                                         const uint8_t* __restrict__ W,
                                                         float* __restrict__ y,
@@ -589,157 +747,180 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   const int kb0 = slice * nbs;
   const int nbw = min(nbs, nb - kb0);
   const int waves = (int)blockDim.x >> 6;
-  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform per wave
+  const int lane = (int)threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int tile = (int)blockIdx.x * waves + wave;
-  const int n0 = min(tile, ntiles - 1) * 16;
-  const int n = tile * 16 + r;
-  const uint8_t* wave_base = W + ((size_t)n0 * nb + kb0) * kBlockBytes;
+  const int tile_step = (int)gridDim.x * waves;
+  const int first = (int)blockIdx.x * waves + wave;
+  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
+  const int total = first < ntiles ? ((ntiles - 1 - first) / tile_step + 1) * nstages : 0;
+  const size_t row_bytes = (size_t)nb * kBlockBytes;
+  const uint8_t* slice_base = W + (size_t)kb0 * kBlockBytes;
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
   const uint32_t wbuf = (uint32_t)(lds_wbuf_base(M, xs_m, ss_m) + wave * 16 * kBufRowStride);
-  StageLane sl;
-  stage_lane(lane, nb, n0, N, wbuf, sl);
   const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
+  const float rcp = 1.0f / (float)M;
   StageBatch sb;
-  stage_issue(st, 0, sb);
-  StageRegs sr;
-  stage_load(wave_base, sl, 0, nbw, sr);
-  stage_finish<kUnitLayout>(st, 0, sb);
-  stage_rest<kUnitLayout>(st);
+  const int last_base = tstage_lead(st, rcp, sb);
+  issue_barrier();
+  StageLane sl;
+  stage_lane(lane, nb, 16, wbuf, sl);
+  StageRegs sr[R];
+  StreamPos ld{first, 0, total - 1};
+  if (total > 0) {
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
+                   sr[u]);
+  }
+  tstage_finish(st, last_base, sb);
   __syncthreads();
-  if (tile >= ntiles) return;
+  tstage_sums(st, rcp);
+  __syncthreads();
 
   const HeaderLane hl = header_lane(g);
-  // A-operand rows this lane reads. An MFMA output row depends only on its A
-  // row, and rows past M are never stored, so those lanes read arbitrary
-  // in-bounds data: staged row 0 shifted by 16 B per lane, which keeps the 16
-  // lanes of a read at distinct addresses (a shared address serializes).
+  // A-operand row this lane reads in each 16-row MFMA tile. An MFMA output row
+  // depends only on its A row and rows past M are never stored, so padded
+  // rows re-read a real row of the same tile.
   const char* xa[MT];
   const float* sa[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int mr = 16 * mt + r;
-    const bool real = mr < M;
-    xa[mt] = lds_x + (real ? mr * xs_m : 16 * (mr - M)) + g * kLdsPairStride;
-    sa[mt] = lds_s + (real ? mr * ss_m : 2 * (mr - M)) + 2 * g;
+    const int rows = min(M - 16 * mt, 16);
+    const int m = 16 * mt + r % rows;
+    xa[mt] = lds_x + 16 * (g * M + m);
+    sa[mt] = lds_s + 2 * (g * M + m);
   }
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
-  f4_t acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
-  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
-  for (int s = 0; s < nstages; ++s) {
-    stage_store(lds, sl, sr);
-    if (s + 1 < nstages) stage_load(wave_base, sl, s + 1, nbw, sr);
-#pragma unroll
-    for (int j = 0; j < kStageBlocks; ++j) {
-      const int bl = s * kStageBlocks + j;
-      if (bl < nbw) {
-        BlockRegs br;
-        read_block(rowbuf, g, j, br);
-        tiled_block<MT>(br, hl, xa, sa, bl, acc);
-      }
-    }
-  }
   const int splits = (int)gridDim.y;
-  if (splits == 1) {
-    if (n < N) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * mt + 4 * g + i;
-          if (m < M) y[(size_t)m * N + n] = acc[mt][i];
-        }
-    }
-    return;
-  }
   const size_t mn = (size_t)M * (size_t)N;
-  if (n < N) {
+  int tile = first, cs = 0;
+  f4_t acc[MT];
+  for (int t = 0; t < total; t += R) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int u = 0; u < R; ++u) {
+      stage_store(lds, sl, sr[u]);
+      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
+                   sr[u]);
+      if (t + u < total) {
+        if (cs == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * g + i;
-        if (m < M) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, acc[mt][i]);
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+// block j+1's LDS reads are issued before block j is computed (the buffer
+        // holds the whole stage; past the slice end they read unused chunks)
+        BlockRegs br[2];
+        read_block(rowbuf, g, 0, br[0]);
+#pragma unroll
+        for (int j = 0; j < kStageBlocks; ++j) {
+          const int bl = cs * kStageBlocks + j;
+          if (j + 1 < kStageBlocks) read_block(rowbuf, g, j + 1, br[(j + 1) & 1]);
+          if (bl < nbw) tiled_block<MT>(br[j & 1], hl, xa, sa, bl, M, acc);
+        }
+        if (++cs == nstages) {
+          const int n = tile * 16 + r;
+          if (splits == 1) {
+            if (n < N) {
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int m = 16 * mt + 4 * g + i;
+                  if (m < M) y[(size_t)m * N + n] = acc[mt][i];
+                }
+            }
+          } else {
+            if (n < N) {
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int m = 16 * mt + 4 * g + i;
+                  if (m < M) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, acc[mt][i]);
+                }
+            }
+            if (arrive_last(counters + tile, splits, lane) && n < N) {
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int m = 16 * mt + 4 * g + i;
+                  if (m < M)
+                    y[(size_t)m * N + n] =
+                        sum_slices(ws, mn, splits, slice, acc[mt][i], (size_t)m * N + n);
+                }
+            }
+          }
+          cs = 0;
+          tile += tile_step;
+        }
       }
-  }
-  if (arrive_last(counters + tile, splits, lane) && n < N) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * g + i;
-        if (m < M)
-          y[(size_t)m * N + n] = sum_slices(ws, mn, splits, slice, acc[mt][i], (size_t)m * N + n);
-      }
+    }
   }
 }
 
-template <int M>
-hipError_t launch_vector(const Launch& a, hipStream_t stream) {
-  dim3 grid(a.grid_x, a.splits), block(64 * a.waves_per_wg);
-  hipLaunchKernelGGL(qmm_vector_kernel<M>, grid, block, a.lds_bytes, stream, a.x,
-                     static_cast<const uint8_t*>(a.W), a.y, a.ws, a.counters, a.N, a.K, a.nbs,
-                     a.xs_m, a.ss_m);
-  return hipGetLastError();
+// Entry points: [ring depth - 1][rows - 1] for the row-vector kernel,
+// [ring depth - 1][MFMA row tiles - 1] for the tiled kernel.
+#define QMM_V(m, r) reinterpret_cast<const void*>(&qmm_vector_kernel<m, r>)
+#define QMM_V8(b, r) QMM_V(b + 1, r), QMM_V(b + 2, r), QMM_V(b + 3, r), QMM_V(b + 4, r), \
+                     QMM_V(b + 5, r), QMM_V(b + 6, r), QMM_V(b + 7, r), QMM_V(b + 8, r)
+const void* const kVectorFn[kMaxRing][32] = {
+    {QMM_V8(0, 1), QMM_V8(8, 1), QMM_V8(16, 1), QMM_V8(24, 1)},
+    {QMM_V8(0, 2), QMM_V8(8, 2), QMM_V8(16, 2), QMM_V8(24, 2)}};
+#undef QMM_V8
+#undef QMM_V
+const void* const kTiledFn[kMaxRing][2] = {
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, 1>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, 1>)},
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, 2>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, 2>)}};
+
+const void* kernel_fn(int kernel, int M, int ring) {
+  if (ring < 1 || ring > kMaxRing || M < 1 || M > 32) return nullptr;
+  return kernel == 2 ? kTiledFn[ring - 1][M > 16 ? 1 : 0] : kVectorFn[ring - 1][M - 1];
 }
-
-template <int MT>
-hipError_t launch_tiled(const Launch& a, hipStream_t stream) {
-  dim3 grid(a.grid_x, a.splits), block(64 * a.waves_per_wg);
-  hipLaunchKernelGGL(qmm_tiled_kernel<MT>, grid, block, a.lds_bytes, stream, a.x,
-                     static_cast<const uint8_t*>(a.W), a.y, a.ws, a.counters, a.M, a.N, a.K,
-                     a.nbs, a.xs_m, a.ss_m);
-  return hipGetLastError();
-}
-
-typedef hipError_t (*LaunchFn)(const Launch&, hipStream_t);
-
-constexpr LaunchFn kVector[32] = {
-    launch_vector<1>,  launch_vector<2>,  launch_vector<3>,  launch_vector<4>,
-    launch_vector<5>,  launch_vector<6>,  launch_vector<7>,  launch_vector<8>,
-    launch_vector<9>,  launch_vector<10>, launch_vector<11>, launch_vector<12>,
-    launch_vector<13>, launch_vector<14>, launch_vector<15>, launch_vector<16>,
-    launch_vector<17>, launch_vector<18>, launch_vector<19>, launch_vector<20>,
-    launch_vector<21>, launch_vector<22>, launch_vector<23>, launch_vector<24>,
-    launch_vector<25>, launch_vector<26>, launch_vector<27>, launch_vector<28>,
-    launch_vector<29>, launch_vector<30>, launch_vector<31>, launch_vector<32>};
-
-template <int M>
-hipError_t raise_vector() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_vector_kernel<M>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
-}
-constexpr hipError_t (*kRaiseVector[32])() = {
-    raise_vector<1>,  raise_vector<2>,  raise_vector<3>,  raise_vector<4>,  raise_vector<5>,
-    raise_vector<6>,  raise_vector<7>,  raise_vector<8>,  raise_vector<9>,  raise_vector<10>,
-    raise_vector<11>, raise_vector<12>, raise_vector<13>, raise_vector<14>, raise_vector<15>,
-    raise_vector<16>, raise_vector<17>, raise_vector<18>, raise_vector<19>, raise_vector<20>,
-    raise_vector<21>, raise_vector<22>, raise_vector<23>, raise_vector<24>, raise_vector<25>,
-    raise_vector<26>, raise_vector<27>, raise_vector<28>, raise_vector<29>, raise_vector<30>,
-    raise_vector<31>, raise_vector<32>};
 
 }  // namespace
 
 hipError_t prepare_kernels() {
-  for (int i = 0; i < 32; ++i) {
-    hipError_t e = kRaiseVector[i]();
-    if (e != hipSuccess) return e;
+  for (int r = 0; r < kMaxRing; ++r) {
+    for (int m = 0; m < 32; ++m) {
+      hipError_t e = hipFuncSetAttribute(kVectorFn[r][m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+      if (e != hipSuccess) return e;
+    }
+    for (int t = 0; t < 2; ++t) {
+      hipError_t e = hipFuncSetAttribute(kTiledFn[r][t], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+      if (e != hipSuccess) return e;
+    }
   }
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_tiled_kernel<1>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_tiled_kernel<2>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+  return hipSuccess;
+}
+
+hipError_t resident_per_cu(int kernel, int M, int ring, int waves, int lds_bytes, int* out) {
+  const void* f = kernel_fn(kernel, M, ring);
+  if (!f) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64 * waves, (size_t)lds_bytes);
 }
 
 hipError_t launch(const Launch& a, hipStream_t stream) {
-  if (a.kernel == 2) return a.M > 16 ? launch_tiled<2>(a, stream) : launch_tiled<1>(a, stream);
-  return kVector[a.M - 1](a, stream);
+  const void* f = kernel_fn(a.kernel, a.M, a.ring);
+  if (!f) return hipErrorInvalidValue;
+  const dim3 grid(a.grid_x, a.splits), block(64 * a.waves_per_wg);
+  const uint8_t* W = static_cast<const uint8_t*>(a.W);
+  int M = a.M, N = a.N, K = a.K, nbs = a.nbs, xs_m = a.xs_m, ss_m = a.ss_m;
+  const float* x = a.x;
+  float* y = a.y;
+  float* ws = a.ws;
+  unsigned* counters = a.counters;
+  if (a.kernel == 2) {
+    void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &xs_m, &ss_m};
+    return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
+  }
+  void* args[] = {&x, &W, &y, &ws, &counters, &N, &K, &nbs, &xs_m, &ss_m};
+  return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
 }
 
 }  // namespace qmm

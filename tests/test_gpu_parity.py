@@ -37,10 +37,11 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run(h, x, W, N, K, kernel=sbb.KERNEL_AUTO, shape=(0, 0, 0), fill=np.nan):
+def run(h, x, W, N, K, kernel=sbb.KERNEL_AUTO, shape=(0, 0, 0), fill=np.nan, ring=0):
     M = x.shape[0]
     sbb.qmm_set_kernel(h, kernel)
     sbb.qmm_set_shape(h, *shape)
+    sbb.qmm_set_ring(h, ring)
     try:
         xd, Wd = to_dev(x), to_dev(W.reshape(-1))
         y = torch.full((M, N), fill, dtype=torch.float32, device="cuda")
@@ -50,6 +51,7 @@ def run(h, x, W, N, K, kernel=sbb.KERNEL_AUTO, shape=(0, 0, 0), fill=np.nan):
     finally:
         sbb.qmm_set_kernel(h, sbb.KERNEL_AUTO)
         sbb.qmm_set_shape(h, 0, 0, 0)
+        sbb.qmm_set_ring(h, 0)
 
 
 def check(y, yref, aref, what=""):
@@ -95,7 +97,7 @@ def test_small_vector(h, M, N, K):
 
 
 @pytest.mark.parametrize("N,K", SMALL_NK)
-@pytest.mark.parametrize("M", [8, 9, 13, 16, 17, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 8, 9, 13, 16, 17, 32])
 def test_small_tiled(h, M, N, K):
     x, W = inputs(M, N, K, tag=N + K + M + 7)
     y = run(h, x, W, N, K, kernel=sbb.KERNEL_TILED)
@@ -104,15 +106,18 @@ def test_small_tiled(h, M, N, K):
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 0), (2, 3, 0), (4, 2, 0), (8, 5, 0), (8, 1, 0), (1, 10, 0),
-                                   (4, 7, 500), (8, 4, 63)])
+                                   (4, 7, 500), (8, 4, 63),
+                                   # fewer workgroups than tiles: waves walk several tiles
+                                   (1, 1, 1), (2, 3, 5), (4, 1, 3), (8, 2, 1), (4, 10, 2)])
 @pytest.mark.parametrize("M,kernel", [(5, sbb.KERNEL_VECTOR), (12, sbb.KERNEL_TILED),
-                                      (12, sbb.KERNEL_VECTOR)])
-def test_launch_shapes(h, M, kernel, shape):
+                                      (12, sbb.KERNEL_VECTOR), (3, sbb.KERNEL_TILED)])
+@pytest.mark.parametrize("ring", [1, 2])
+def test_launch_shapes(h, M, kernel, shape, ring):
     N, K = 1000, 2560
     x, W = inputs(M, N, K, tag=31 + M)
-    y = run(h, x, W, N, K, kernel=kernel, shape=shape)
+    y = run(h, x, W, N, K, kernel=kernel, shape=shape, ring=ring)
     yref, aref = oracle.qmm(x, W, N, K)
-    check(y, yref, aref, "M=%d kernel=%d shape=%s" % (M, kernel, shape))
+    check(y, yref, aref, "M=%d kernel=%d shape=%s ring=%d" % (M, kernel, shape, ring))
 
 
 # ------------------------------------------------------------ the workloads
@@ -288,11 +293,11 @@ def test_errors_launch_nothing(h):
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), 33, N, K, s) == sbb.QMM_ERR_SHAPE
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), M, N, 300, s) == sbb.QMM_ERR_SHAPE
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), xd.data_ptr() + 64, M, N, K, s) == sbb.QMM_ERR_OVERLAP
-    sbb.qmm_set_kernel(h, sbb.KERNEL_TILED)
+    sbb.qmm_set_shape(h, 3, 0, 0)  # 3 waves per workgroup is not a launch shape
     try:
         assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), M, N, K, s) == sbb.QMM_ERR_INVALID_ARG
     finally:
-        sbb.qmm_set_kernel(h, sbb.KERNEL_AUTO)
+        sbb.qmm_set_shape(h, 0, 0, 0)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), M, N, K, s) == sbb.QMM_OK
