@@ -145,8 +145,8 @@ class Pass:
     def kernel_symbol(self, M, N, K):
         p = self.plan(M, N, K)
         if p["kernel"] == self.sbb.KERNEL_TILED:
-            return "qmm_tiled_kernel<%d, %d>" % (1 if M <= 16 else 2, p["ring"])
-        return "qmm_vector_kernel<%d, %d>" % (M, p["ring"])
+            return "qmm_tiled_kernel<%d>" % (1 if M <= 16 else 2)
+        return "qmm_vector_kernel<%d>" % M
 
 
 def time_passes(P, steps, warmup, graph):

@@ -122,19 +122,22 @@ enum {
 /* One launch-table entry: which kernel, how the grid is shaped. */
 typedef struct {
   int32_t kernel;        /* QMM_KERNEL_VECTOR or QMM_KERNEL_TILED */
-  int32_t waves_per_wg;  /* wavefronts per workgroup: 1, 2, 4 or 8 */
+  int32_t waves_per_wg;  /* wavefronts per workgroup: 1..8 */
   int32_t splits;        /* K split into this many slices (1 = no split-K) */
-  int32_t grid_x;        /* workgroups per K slice; each wavefront walks the 16-row
-                            tiles b*waves + w, + grid_x*waves, ... of its slice, so
-                            the table never launches more workgroups than the
-                            device holds at once (nor more than one tile per
-                            wavefront needs) */
+  int32_t grid_x;        /* workgroups per range of wave_splits slices; each tile
+                            group of a workgroup walks the 16-row tiles
+                            b*groups + t, + grid_x*groups, ..., so the table never
+                            launches more workgroups than the device holds at
+                            once (nor more than one tile per group needs) */
   int32_t blocks_per_split; /* super-blocks along K per slice */
   int32_t lds_bytes;     /* LDS per workgroup */
-  int32_t ring;          /* weight stages a wavefront keeps in registers: while it
-                            computes one stage from LDS, the loads of ring-1
-                            more are in flight (1 or 2) */
-  int64_t workspace_bytes; /* split-K partials used (0 when splits == 1) */
+  int32_t wave_splits;   /* slices reduced inside one workgroup: its waves form
+                            waves_per_wg / wave_splits tile groups, and the
+                            wave_splits waves of a group sum their slices in LDS;
+                            the remaining splits / wave_splits ranges are
+                            summed across workgroups (split-K) */
+  int64_t workspace_bytes; /* split-K partials used (0 without split-K across
+                              workgroups) */
 } qmm_plan;
 
 /* The entry qmm_run would use for (M, N, K) with the handle's current
@@ -145,18 +148,19 @@ int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out)
  * restores the table). For tests and sweeps. */
 int qmm_set_kernel(qmm_handle h, int kernel);
 
-/* Override the grid shape for every following call: waves_per_wg (0 = table),
- * splits (0 = table), grid_x (0 = table; any positive count works: with fewer
- * workgroups each wavefront walks more tiles, with more some stay idle).
- * Values that do not fit the call (LDS, workspace, K) make qmm_run return
- * QMM_ERR_INVALID_ARG. On a planning-only handle the table's grid_x is one
- * tile per wavefront (the device's capacity is unknown there). For sweeps. */
+/* Override the grid shape for every following call: waves_per_wg (0 = table,
+ * else 1..8), splits (0 = table), grid_x (0 = table; any positive count works:
+ * with fewer workgroups each tile group walks more tiles, with more some stay
+ * idle). Values that do not fit the call (LDS, workspace, K) make qmm_run
+ * return QMM_ERR_INVALID_ARG. On a planning-only handle the table's grid_x is
+ * one tile per tile group (the device's capacity is unknown there). For
+ * sweeps. */
 int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x);
 
-/* Override the register stages of the weight stream for every following
- * call (0 = table, else 1 or 2; other values return QMM_ERR_INVALID_ARG).
- * For sweeps. */
-int qmm_set_ring(qmm_handle h, int ring);
+/* Override how many K slices one workgroup reduces itself for every following
+ * call (0 = table, else 1..8; waves_per_wg must be a multiple and splits at
+ * least this, or qmm_run returns QMM_ERR_INVALID_ARG). For sweeps. */
+int qmm_set_wave_splits(qmm_handle h, int wave_splits);
 
 /* The row count from which the launch table switches from the row-vector to
  * the tiled kernel (M >= switch uses the tiled kernel). */

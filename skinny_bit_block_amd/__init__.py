@@ -29,7 +29,7 @@ KERNEL_AUTO, KERNEL_VECTOR, KERNEL_TILED = 0, 1, 2
 KERNEL_NAMES = {KERNEL_VECTOR: "vector", KERNEL_TILED: "tiled"}
 
 EXPORTS = ["qmm_create", "qmm_run", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
-           "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_ring",
+           "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_wave_splits",
            "qmm_switch_point"]
 
 
@@ -37,7 +37,7 @@ class qmm_plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("grid_x", ctypes.c_int32),
                 ("blocks_per_split", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("ring", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+                ("wave_splits", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -71,8 +71,8 @@ def load():
         lib.qmm_set_kernel.restype = ctypes.c_int
         lib.qmm_set_shape.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.qmm_set_shape.restype = ctypes.c_int
-        lib.qmm_set_ring.argtypes = [vp, ctypes.c_int]
-        lib.qmm_set_ring.restype = ctypes.c_int
+        lib.qmm_set_wave_splits.argtypes = [vp, ctypes.c_int]
+        lib.qmm_set_wave_splits.restype = ctypes.c_int
         lib.qmm_switch_point.argtypes = [vp, i64, i64]
         lib.qmm_switch_point.restype = ctypes.c_int
         _lib = lib
@@ -170,8 +170,8 @@ def qmm_set_shape(h, waves_per_wg=0, splits=0, grid_x=0):
     return _check(load().qmm_set_shape(h, int(waves_per_wg), int(splits), int(grid_x)))
 
 
-def qmm_set_ring(h, ring=0):
-    return _check(load().qmm_set_ring(h, int(ring)))
+def qmm_set_wave_splits(h, wave_splits=0):
+    return _check(load().qmm_set_wave_splits(h, int(wave_splits)))
 
 
 def qmm_switch_point(h, N, K):

@@ -19,7 +19,7 @@
 
 // Cached occupancy query: workgroups per compute unit for one launch shape.
 struct qmm_occ {
-  int kernel, M, ring, waves, lds, wgs;
+  int kernel, M, waves, lds, wgs;
 };
 
 struct qmm_ctx {
@@ -28,7 +28,7 @@ struct qmm_ctx {
   qmm_occ occ[64];      // small cache of occupancy queries (launch shapes seen)
   int nocc;
   int forced_kernel;    // QMM_KERNEL_*
-  int force_waves, force_splits, force_grid, force_ring;
+  int force_waves, force_splits, force_grid, force_wsplit;
   float* ws;            // split-K partials
   int64_t ws_bytes;
   unsigned* counters;   // split-K arrival counters, one per row tile, zeroed at creation
@@ -39,7 +39,6 @@ namespace {
 constexpr int64_t kWorkspaceBytes = 128ll << 20;
 constexpr int kGfx950Cus = 256;
 constexpr int kDefaultWaves = 4;
-constexpr int kDefaultRing = 1;
 // Split K until there are at least this many row tiles of work (a wave per
 // tile); below that the chip cannot keep enough loads in flight.
 constexpr int64_t kTargetTiles = 1024;
@@ -53,29 +52,31 @@ int check_shape(int64_t M, int64_t N, int64_t K) {
 }
 
 // Measured entries of the launch table (gfx950, MI355X): the fastest
-// (kernel, waves per workgroup, K slices) of a sweep over those three, timed
+// (kernel, waves per workgroup, K slices, slices per workgroup) of a sweep, timed
 // on the distinct matrices of a model pass in sequence (cold weights), per
 // matrix shape of the pass and per range of rows; rows between measured
 // points take the entry below them.
 struct TableEntry {
-  int32_t N, K, m_lo, kernel, waves, splits;
+  int32_t N, K, m_lo, kernel, waves, splits, wsplit;
 };
 constexpr TableEntry kTable[] = {
     // 5120 x 5120 projections
-    {5120, 5120, 1, QMM_KERNEL_VECTOR, 4, 5},
-    {5120, 5120, 2, QMM_KERNEL_TILED, 4, 3},
+    {5120, 5120, 1, QMM_KERNEL_VECTOR, 4, 5, 2},
+    {5120, 5120, 2, QMM_KERNEL_VECTOR, 4, 5, 1},
+    {5120, 5120, 5, QMM_KERNEL_TILED, 4, 3, 1},
     // gate+up, N = 2 x 17408
-    {34816, 5120, 1, QMM_KERNEL_VECTOR, 4, 1},
-    {34816, 5120, 2, QMM_KERNEL_TILED, 4, 1},
-    {34816, 5120, 16, QMM_KERNEL_TILED, 8, 2},
+    {34816, 5120, 1, QMM_KERNEL_VECTOR, 4, 2, 2},
+    {34816, 5120, 2, QMM_KERNEL_TILED, 4, 1, 1},
+    {34816, 5120, 16, QMM_KERNEL_TILED, 8, 2, 1},
     // down
-    {5120, 17408, 1, QMM_KERNEL_VECTOR, 4, 5},
-    {5120, 17408, 2, QMM_KERNEL_TILED, 4, 3},
-    {5120, 17408, 16, QMM_KERNEL_TILED, 4, 5},
+    {5120, 17408, 1, QMM_KERNEL_VECTOR, 4, 5, 1},
+    {5120, 17408, 2, QMM_KERNEL_TILED, 4, 3, 1},
+    {5120, 17408, 8, QMM_KERNEL_TILED, 8, 5, 1},
+    {5120, 17408, 16, QMM_KERNEL_TILED, 4, 5, 1},
     // lm_head
-    {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1},
-    {151936, 5120, 2, QMM_KERNEL_TILED, 4, 1},
-    {151936, 5120, 16, QMM_KERNEL_TILED, 8, 2},
+    {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1, 1},
+    {151936, 5120, 2, QMM_KERNEL_TILED, 4, 1, 1},
+    {151936, 5120, 16, QMM_KERNEL_TILED, 8, 2, 1},
 };
 
 // The entry for (M, N, K), or nullptr when the shape is not in the table.
@@ -86,35 +87,39 @@ const TableEntry* table_entry(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
-// Shapes outside the table: the row-vector kernel for one row, the tiled
-// kernel from two rows on (where the sweeps put the switch for every shape).
+// The row count from which the launch table uses the tiled kernel: for a
+// shape in the table the first entry that does; elsewhere two rows (where the
+// sweeps put the switch for most shapes).
 int table_switch(int64_t N, int64_t K) {
-  const TableEntry* e1 = table_entry(1, N, K);
-  if (e1 && e1->kernel == QMM_KERNEL_TILED) return 1;
-  return 2;
+  for (int m = 1; m <= QMM_MAX_M; ++m) {
+    const TableEntry* e = table_entry(m, N, K);
+    if (!e) return 2;
+    if (e->kernel == QMM_KERNEL_TILED) return m;
+  }
+  return QMM_MAX_M + 1;
 }
 
 // Workgroups of one launch shape the whole device holds at once; 0 when
 // unknown (planning-only handle, or the query failed).
-int64_t resident(qmm_ctx* h, int kernel, int M, int ring, int waves, int lds) {
+int64_t resident(qmm_ctx* h, int kernel, int M, int waves, int lds) {
   if (h->device < 0) return 0;
   for (int i = 0; i < h->nocc; ++i) {
     const qmm_occ& o = h->occ[i];
-    if (o.kernel == kernel && o.M == M && o.ring == ring && o.waves == waves && o.lds == lds)
+    if (o.kernel == kernel && o.M == M && o.waves == waves && o.lds == lds)
       return (int64_t)o.wgs * h->cus;
   }
   int prev = 0, wgs = 0;
   if (hipGetDevice(&prev) != hipSuccess) return 0;
   const bool sw = prev != h->device;
   if (sw && hipSetDevice(h->device) != hipSuccess) return 0;
-  const hipError_t e = qmm::resident_per_cu(kernel, M, ring, waves, lds, &wgs);
+  const hipError_t e = qmm::resident_per_cu(kernel, M, waves, lds, &wgs);
   if (sw) (void)hipSetDevice(prev);
   if (e != hipSuccess || wgs < 1) {
     (void)hipGetLastError();
     return 0;
   }
   const int slot = h->nocc < 64 ? h->nocc++ : (int)((uint32_t)(kernel * 131 + M * 31 + waves * 7 + lds) % 64u);
-  h->occ[slot] = qmm_occ{kernel, M, ring, waves, lds, wgs};
+  h->occ[slot] = qmm_occ{kernel, M, waves, lds, wgs};
   return (int64_t)wgs * h->cus;
 }
 
@@ -130,19 +135,19 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
 
   const int waves = h->force_waves ? h->force_waves
                                    : (te ? te->waves : (ntiles >= 4096 ? 8 : kDefaultWaves));
-  const int ring = h->force_ring ? h->force_ring : kDefaultRing;
-  if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return QMM_ERR_INVALID_ARG;
+  if (waves < 1 || waves > qmm::kMaxWavesPerWg) return QMM_ERR_INVALID_ARG;
+  int wsplit = h->force_wsplit ? h->force_wsplit : (te ? te->wsplit : 1);
+  if (!h->force_wsplit && waves % wsplit) wsplit = 1;
+  if (wsplit < 1 || waves % wsplit) return QMM_ERR_INVALID_ARG;
 
+  // K slices: the table's count, or enough tile-slices to fill the chip while
+  // keeping at least a stage of super-blocks per slice; then raised until the
+  // workgroup's staged x (wsplit slices) fits in LDS.
   int splits;
   if (h->force_splits) {
     splits = h->force_splits;
     if (splits < 1 || splits > nb) return QMM_ERR_INVALID_ARG;
   } else {
-    // fewest slices whose activations fit in LDS ...
-    int s_lds = 1;
-    while (s_lds < nb && qmm::lds_bytes((int)M, (nb + s_lds - 1) / s_lds, waves, kernel) > qmm::kLdsMax) ++s_lds;
-    // ... and enough row-tile work items to fill the chip, keeping at least a
-    // ring's worth of super-blocks per slice
     int s_par = 1;
     if (te) {
       s_par = te->splits < nb ? te->splits : nb;
@@ -151,24 +156,32 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
              ntiles <= qmm::kMaxCounterTiles)
         ++s_par;
     }
-    splits = s_lds > s_par ? s_lds : s_par;
+    splits = s_par < wsplit ? wsplit : s_par;
+    while (splits < nb &&
+           qmm::lds_bytes((int)M, wsplit * ((nb + splits - 1) / splits), waves, wsplit, kernel) >
+               qmm::kLdsMax)
+      ++splits;
   }
+  if (splits < wsplit) return QMM_ERR_INVALID_ARG;
   const int nbs = (nb + splits - 1) / splits;
   splits = (nb + nbs - 1) / nbs;  // no empty slice
-  const int lds = qmm::lds_bytes((int)M, nbs, waves, kernel);
+  const int grid_y = (splits + wsplit - 1) / wsplit;
+  const int lds = qmm::lds_bytes((int)M, wsplit * nbs, waves, wsplit, kernel);
   if (lds > qmm::kLdsMax) return QMM_ERR_INVALID_ARG;
-  const int64_t ws = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+  const int64_t ws = grid_y > 1 ? (int64_t)grid_y * M * N * 4 : 0;
   if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
-  if (splits > 1 && ntiles > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
+  if (grid_y > 1 && ntiles > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
 
-  // at most one row tile per wavefront, and no more workgroups than the device
-  // holds at once: the waves then walk several tiles each (persistent grid)
-  const int64_t need = (ntiles + waves - 1) / waves;
+  // at most one row tile per tile group of wsplit waves, and no more
+  // workgroups than the device holds at once: the waves then walk several
+  // tiles each (persistent grid)
+  const int groups = waves / wsplit;
+  const int64_t need = (ntiles + groups - 1) / groups;
   int64_t grid = need;
-  const int64_t res = resident(h, kernel, (int)M, ring, waves, lds);
+  const int64_t res = resident(h, kernel, (int)M, waves, lds);
   if (res > 0) {
-    const int64_t per_slice = res / splits > 0 ? res / splits : 1;
-    if (per_slice < grid) grid = per_slice;
+    const int64_t per_range = res / grid_y > 0 ? res / grid_y : 1;
+    if (per_range < grid) grid = per_range;
   }
   if (h->force_grid) grid = h->force_grid;
   if (grid > 0x7FFFFFFF) return QMM_ERR_INVALID_ARG;
@@ -177,9 +190,9 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   p->waves_per_wg = waves;
   p->splits = splits;
   p->grid_x = (int32_t)grid;
-  p->ring = ring;
   p->blocks_per_split = nbs;
   p->lds_bytes = lds;
+  p->wave_splits = wsplit;
   p->workspace_bytes = ws;
   return QMM_OK;
 }
@@ -306,9 +319,9 @@ int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x) {
   return QMM_OK;
 }
 
-int qmm_set_ring(qmm_handle h, int ring) {
-  if (!h || ring < 0 || ring > qmm::kMaxRing) return QMM_ERR_INVALID_ARG;
-  h->force_ring = ring;
+int qmm_set_wave_splits(qmm_handle h, int wave_splits) {
+  if (!h || wave_splits < 0 || wave_splits > qmm::kMaxWavesPerWg) return QMM_ERR_INVALID_ARG;
+  h->force_wsplit = wave_splits;
   return QMM_OK;
 }
 
@@ -339,12 +352,12 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_
   a.N = (int)N;
   a.K = (int)K;
   a.waves_per_wg = p.waves_per_wg;
-  a.splits = p.splits;
+  a.wsplit = p.wave_splits;
   a.grid_x = p.grid_x;
-  a.ring = p.ring;
+  a.grid_y = (p.splits + p.wave_splits - 1) / p.wave_splits;
   a.nbs = p.blocks_per_split;
-  a.xs_m = qmm::lds_xs_m(p.blocks_per_split, p.kernel);
-  a.ss_m = qmm::lds_ss_m(p.blocks_per_split, p.kernel);
+  a.xs_m = qmm::lds_xs_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.ss_m = qmm::lds_ss_m(p.wave_splits * p.blocks_per_split, p.kernel);
   a.lds_bytes = p.lds_bytes;
   a.x = x;
   a.W = W_blocks;

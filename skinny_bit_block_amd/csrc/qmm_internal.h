@@ -13,23 +13,22 @@ constexpr int kBlockBytes = 144;    // bytes per super-block
 // where a unit goes (see the kernel file).
 constexpr int kLdsMax = 160 * 1024;  // LDS a workgroup may allocate on gfx950
 constexpr int kMaxWavesPerWg = 8;
-constexpr int kMaxRing = 2;  // register stages of the weight stream a kernel may keep
 
 struct Launch {
   int kernel;       // 1 = row-vector, 2 = tiled (MFMA)
   int M, N, K;
   int waves_per_wg;
-  int splits;       // K slices (grid.y)
-  int grid_x;       // workgroups per slice
-  int ring;         // register stages of the weight stream (1..kMaxRing)
-  int nbs;          // super-blocks per slice
+  int wsplit;       // K slices reduced inside one workgroup (waves_per_wg % wsplit == 0)
+  int grid_x;       // workgroups per slice range
+  int grid_y;       // slice ranges (split-K across workgroups when > 1)
+  int nbs;          // super-blocks per K slice
   int xs_m;         // LDS bytes per staged activation row
   int ss_m;         // floats per row of staged sub-block sums
   int lds_bytes;
   const float* x;
   const void* W;
   float* y;
-  float* ws;        // split-K partials [splits][M][N] (splits > 1)
+  float* ws;        // split-K partials [grid_y][M][N] (grid_y > 1)
   unsigned* counters;  // split-K arrival counter per row tile, zero between calls
 };
 
@@ -46,13 +45,18 @@ inline int lds_ss_m(int nbw, int kernel) { return kernel == 1 ? nbw * 8 + 2 : nb
 // Per-wavefront transpose buffer of the weight stream: 16 rows x (4 blocks =
 // 36 chunks of 16 B + one chunk of padding).
 constexpr int kWaveBufBytes = 16 * 16 * 37;
-// The per-wave weight buffers start 16-byte aligned after the staged
-// activations and sub-block sums.
-__host__ __device__ inline int lds_wbuf_base(int M, int xs_m, int ss_m) {
+// LDS of a workgroup: staged x, sub-block sums, then (16-byte aligned) the
+// buffer of the in-workgroup reduction when wsplit > 1 (two iterations' worth,
+// 16 floats per row m, tile group and slice), then the per-wave weight buffers.
+__host__ __device__ inline int lds_red_base(int M, int xs_m, int ss_m) {
   return (M * xs_m + M * ss_m * 4 + 15) & ~15;
 }
-inline int lds_bytes(int M, int nbw, int waves, int kernel) {
-  return lds_wbuf_base(M, lds_xs_m(nbw, kernel), lds_ss_m(nbw, kernel)) + waves * kWaveBufBytes;
+__host__ __device__ inline int lds_red_bytes(int M, int waves, int wsplit) {
+  return wsplit > 1 ? 2 * waves * M * 16 * 4 : 0;
+}
+inline int lds_bytes(int M, int nbw, int waves, int wsplit, int kernel) {
+  return lds_red_base(M, lds_xs_m(nbw, kernel), lds_ss_m(nbw, kernel)) +
+         lds_red_bytes(M, waves, wsplit) + waves * kWaveBufBytes;
 }
 
 hipError_t launch(const Launch& a, hipStream_t stream);
@@ -60,6 +64,6 @@ hipError_t prepare_kernels();  // raise the dynamic-LDS limit of every kernel
 // Workgroups of the kernel a launch with these parameters uses that one
 // compute unit holds at once (registers, LDS and wave slots), on the current
 // device.
-hipError_t resident_per_cu(int kernel, int M, int ring, int waves, int lds_bytes, int* out);
+hipError_t resident_per_cu(int kernel, int M, int waves, int lds_bytes, int* out);
 
 }  // namespace qmm

@@ -369,37 +369,108 @@ __device__ __forceinline__ float sum_slices(const float* ws, size_t mn, int spli
   return v;
 }
 
-// A wave's work is a stream of (tile, stage) elements: its tiles in order, each
-// in nstages stages of its K slice. R register stages are kept: while the
-// wave computes one element from LDS, the loads of the next R-1 are in
-// flight, across tile boundaries. Element e uses register stage e mod R; the
-// loop is unrolled by R so that the register stage is static, and the stream
-// is padded to a multiple of R. With R > 1 every step issues its loads (past
-// the end they re-read the last element), so that the wait before each use is
-// the same static count on every path; with R = 1 only real elements are
-// loaded (a wave cannot finish while loads are outstanding, so a padded load
-// would add a memory round trip to every wave's end).
-struct StreamPos {
-  int tile, s;  // next element whose loads are to be issued
-  int left;     // elements after it in the stream; -1 once it is past the end
+// Work split inside a workgroup. Its waves form T = waves / wsplit tile groups
+// of wsplit waves; the waves of a group reduce consecutive K slices of the same
+// row tile, and their partial sums meet in LDS (in slice order, after a
+// barrier) instead of in global memory. The workgroups of one slice range walk
+// the row tiles round-robin; every wave of a workgroup runs the same number of
+// tile iterations, so the barrier is uniform.
+struct Split {
+  int wslice, wtile, T;  // this wave's slice within the workgroup, its tile group, groups
+  int kb0, nbw;          // this wave's K slice: first super-block, count (may be 0)
+  int bl_off;            // its first super-block within the workgroup's staged x
+  int kb0_wg, nbw_wg;    // the workgroup's K range
+  int iters;             // tile iterations of the workgroup
 };
 
-template <int R>
-__device__ __forceinline__ void stream_issue(const uint8_t* slice_base, size_t row_bytes, int N,
-                                             int nb, int nbw, int nstages, int tile_step, int lane,
-                                             uint32_t wbuf, StageLane& sl, StreamPos& p,
-                                             StageRegs& dst) {
-  if (R == 1 && p.left < 0) return;
-  if (p.s == 0 && N - p.tile * 16 < 16) stage_lane(lane, nb, N - p.tile * 16, wbuf, sl);
-  stage_load(slice_base + (size_t)p.tile * 16 * row_bytes, sl, p.s, nbw, dst);
-  if (p.left > 0) {
-    if (++p.s == nstages) {
-      p.s = 0;
-      p.tile += tile_step;
+__device__ __forceinline__ Split make_split(int wave, int waves, int wsplit, int nbs, int nb,
+                                            int ntiles) {
+  Split c;
+  c.wslice = wave % wsplit;
+  c.wtile = wave / wsplit;
+  c.T = waves / wsplit;
+  c.kb0_wg = (int)blockIdx.y * wsplit * nbs;
+  c.nbw_wg = min(wsplit * nbs, nb - c.kb0_wg);
+  c.bl_off = c.wslice * nbs;
+  c.kb0 = c.kb0_wg + c.bl_off;
+  c.nbw = max(0, min(nbs, nb - c.kb0));
+  const int first_wg = (int)blockIdx.x * c.T;
+  const int step = (int)gridDim.x * c.T;
+  c.iters = first_wg < ntiles ? (ntiles - 1 - first_wg) / step + 1 : 0;
+  return c;
+}
+
+// LDS buffer of the in-workgroup reduction: floats [parity][tile group][slice][m][16],
+// parity = iteration & 1 (one barrier per iteration then suffices).
+__device__ __forceinline__ float* red_slot(float* red, int par, const Split& c, int wsplit,
+                                           int slice, int M) {
+  return red + (size_t)(((par * c.T + c.wtile) * wsplit + slice) * M) * 16;
+}
+
+// Output of one row tile: NV values per lane, for rows mrow[k] (ok[k]: row < M)
+// of output column n. Writes y, or with split-K across workgroups the partial
+// and, for the last slice to arrive, the sum of all slices in slice order.
+template <int NV>
+__device__ __forceinline__ void write_tile(const float (&v)[NV], const int (&mrow)[NV],
+                                           const bool (&ok)[NV], int n, int N, int M, int tile,
+                                           float* __restrict__ y, float* __restrict__ ws,
+                                           unsigned* __restrict__ counters, int lane) {
+  const int gsplits = (int)gridDim.y, gslice = (int)blockIdx.y;
+  if (gsplits == 1) {
+    if (n < N) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (ok[k]) y[(size_t)mrow[k] * N + n] = v[k];
     }
+    return;
   }
-  --p.left;
-  if (R > 1 && p.left < 0) p.left = 0;
+  const size_t mn = (size_t)M * (size_t)N;
+  if (n < N) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (ok[k]) store_partial(ws + (size_t)gslice * mn + (size_t)mrow[k] * N + n, v[k]);
+  }
+  if (arrive_last(counters + tile, gsplits, lane) && n < N) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (ok[k])
+        y[(size_t)mrow[k] * N + n] =
+            sum_slices(ws, mn, gsplits, gslice, v[k], (size_t)mrow[k] * N + n);
+  }
+}
+
+// One tile iteration's end: with wsplit > 1 the slices' partials meet in LDS
+// and the tile group's first wave writes the tile. Every wave of the workgroup
+// calls this once per iteration (it contains the barrier).
+template <int NV>
+__device__ __forceinline__ void finish_tile(float (&v)[NV], const int (&mrow)[NV],
+                                            const bool (&ok)[NV], bool valid, int it,
+                                            const Split& c, int wsplit, float* red, int r,
+                                            int n, int N, int M, int tile, float* __restrict__ y,
+                                            float* __restrict__ ws, unsigned* __restrict__ counters,
+                                            int lane) {
+  if (wsplit == 1) {
+    if (valid) write_tile<NV>(v, mrow, ok, n, N, M, tile, y, ws, counters, lane);
+    return;
+  }
+  const int par = it & 1;
+  if (valid) {
+    float* mine = red_slot(red, par, c, wsplit, c.wslice, M);
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (ok[k]) mine[mrow[k] * 16 + r] = v[k];
+  }
+  __syncthreads();
+  if (valid && c.wslice == 0) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!ok[k]) continue;
+      float sum = v[k];  // slice 0 is this wave's own
+      for (int sl = 1; sl < wsplit; ++sl) sum += red_slot(red, par, c, wsplit, sl, M)[mrow[k] * 16 + r];
+      v[k] = sum;
+    }
+    write_tile<NV>(v, mrow, ok, n, N, M, tile, y, ws, counters, lane);
+  }
 }
 
 // ---------------------------------------------------------------- row-vector
@@ -479,50 +550,43 @@ __device__ __forceinline__ void vector_block(const BlockRegs& br, const HeaderLa
 // compute, are not queued behind a whole stage of weight streams.
 __device__ __forceinline__ void issue_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// The workgroups of a K slice share its row tiles round-robin: wave w of
-// workgroup b takes tiles b*waves + w, then + gridDim.x*waves, and so on, so a
-// grid no larger than what the chip holds at once stages x once per
-// workgroup.
-template <int M, int R>
+template <int M>
 __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict__ x,
                                                          const uint8_t* __restrict__ W,
                                                          float* __restrict__ y,
                                                          float* __restrict__ ws,
                                                          unsigned* __restrict__ counters, int N,
-                                                         int K, int nbs, int xs_m, int ss_m) {
+                                                         int K, int nbs, int wsplit, int xs_m,
+                                                         int ss_m) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int nb = K / kBlockWeights;
-  const int slice = (int)blockIdx.y;
-  const int kb0 = slice * nbs;
-  const int nbw = min(nbs, nb - kb0);
   const int waves = (int)blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform per wave
   const int lane = (int)threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int tile_step = (int)gridDim.x * waves;
-  const int first = (int)blockIdx.x * waves + wave;
-  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
-  const int total = first < ntiles ? ((ntiles - 1 - first) / tile_step + 1) * nstages : 0;
+  const Split c = make_split(wave, waves, wsplit, nbs, nb, ntiles);
+  const int tile_step = (int)gridDim.x * c.T;
+  const int nstages = (c.nbw + kStageBlocks - 1) / kStageBlocks;
   const size_t row_bytes = (size_t)nb * kBlockBytes;
-  const uint8_t* slice_base = W + (size_t)kb0 * kBlockBytes;
+  const uint8_t* slice_base = W + (size_t)c.kb0 * kBlockBytes;
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
-  const uint32_t wbuf = (uint32_t)(lds_wbuf_base(M, xs_m, ss_m) + wave * 16 * kBufRowStride);
-  const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
+  const int red_base = lds_red_base(M, xs_m, ss_m);
+  float* red = reinterpret_cast<float*>(lds + red_base);
+  const uint32_t wbuf =
+      (uint32_t)(red_base + lds_red_bytes(M, waves, wsplit) + wave * 16 * kBufRowStride);
+  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s};
   StageBatch sb;
   stage_issue(st, 0, sb);
   issue_barrier();
+  int tile = (int)blockIdx.x * c.T + c.wtile;
   StageLane sl;
-  stage_lane(lane, nb, 16, wbuf, sl);
-  StageRegs sr[R];
-  StreamPos ld{first, 0, total - 1};
-  if (total > 0) {
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
-                   sr[u]);
+  StageRegs sr;
+  if (tile < ntiles && nstages > 0) {
+    stage_lane(lane, nb, min(16, N - tile * 16), wbuf, sl);
+    stage_load(slice_base + (size_t)tile * 16 * row_bytes, sl, 0, c.nbw, sr);
   }
   stage_finish(st, 0, sb);
   stage_rest(st);
@@ -532,65 +596,64 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
   const char* xl = lds_x + g * 128 + 8 * r;
   const float* sg = lds_s + 2 * g;
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
-  const int splits = (int)gridDim.y;
-  const size_t mn = (size_t)M * (size_t)N;
-  int tile = first, cs = 0;
+  constexpr int NV = (M + 3) / 4;  // rows m = g + 4k of this lane's outputs
+  int mrow[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    mrow[k] = min(g + 4 * k, M - 1);
+    ok[k] = g + 4 * k < M;
+  }
+  // one flat loop over (tile, stage) steps with a single load site; a wave
+  // without K work takes one empty step per tile, so every wave reaches
+  // finish_tile (and its barrier) once per tile iteration
+  const int ns = max(nstages, 1);
+  const int total = c.iters * ns;
+  int cs = 0, it = 0;
   float acc[M];
-  for (int t = 0; t < total; t += R) {
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      stage_store(lds, sl, sr[u]);
-      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
-                   sr[u]);
-      if (t + u < total) {
-        if (cs == 0) {
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (int e = 0; e < total; ++e) {
+    const bool valid = tile < ntiles;
+    if (valid && nstages > 0) {
+      stage_store(lds, sl, sr);
+      int nt = tile, nsn = cs + 1;
+      if (nsn == nstages) {
+        nsn = 0;
+        nt += tile_step;
+      }
+      if (nt < ntiles) {
+        if (nsn == 0 && N - nt * 16 < 16) stage_lane(lane, nb, N - nt * 16, wbuf, sl);
+        stage_load(slice_base + (size_t)nt * 16 * row_bytes, sl, nsn, c.nbw, sr);
+      }
 #pragma unroll
-          for (int m = 0; m < M; ++m) acc[m] = 0.f;
-        }
-// block j+1's LDS reads are issued before block j is computed (the buffer
-        // holds the whole stage; past the slice end they read unused chunks)
-        BlockRegs br[2];
-        read_block(rowbuf, g, 0, br[0]);
-#pragma unroll
-        for (int j = 0; j < kStageBlocks; ++j) {
-          const int bl = cs * kStageBlocks + j;
-          if (j + 1 < kStageBlocks) read_block(rowbuf, g, j + 1, br[(j + 1) & 1]);
-          if (bl < nbw) vector_block<M>(br[j & 1], hl, xl, sg, bl, xs_m, ss_m, acc);
-        }
-        if (++cs == nstages) {
-          // the four lanes of a row (g = 0..3) hold its four j-pair partials
-          float out[M];
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float v = acc[m];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            out[m] = v;
-          }
-          const int n = tile * 16 + r;
-          if (splits == 1) {
-            if (n < N) {
-#pragma unroll
-              for (int m = 0; m < M; ++m)
-                if ((m & 3) == g) y[(size_t)m * N + n] = out[m];
-            }
-          } else {
-            if (n < N) {
-#pragma unroll
-              for (int m = 0; m < M; ++m)
-                if ((m & 3) == g) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, out[m]);
-            }
-            if (arrive_last(counters + tile, splits, lane) && n < N) {
-#pragma unroll
-              for (int m = 0; m < M; ++m)
-                if ((m & 3) == g)
-                  y[(size_t)m * N + n] = sum_slices(ws, mn, splits, slice, out[m], (size_t)m * N + n);
-            }
-          }
-          cs = 0;
-          tile += tile_step;
+      for (int j = 0; j < kStageBlocks; ++j) {
+        const int bl = cs * kStageBlocks + j;
+        if (bl < c.nbw) {
+          BlockRegs br;
+          read_block(rowbuf, g, j, br);
+          vector_block<M>(br, hl, xl, sg, c.bl_off + bl, xs_m, ss_m, acc);
         }
       }
+    }
+    if (++cs == ns) {
+      // the four lanes of a row (g = 0..3) hold its four j-pair partials
+      float v[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[k] = 0.f;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float t = acc[m];
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        if ((m & 3) == g) v[m >> 2] = t;
+        acc[m] = 0.f;
+      }
+      finish_tile<NV>(v, mrow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, tile, y, ws,
+                      counters, lane);
+      cs = 0;
+      ++it;
+      tile += tile_step;
     }
   }
 }
@@ -733,48 +796,44 @@ __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLan
   }
 }
 
-template <int MT, int R>
+template <int MT>
 __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict__ x,
                                                         const uint8_t* __restrict__ W,
                                                         float* __restrict__ y,
                                                         float* __restrict__ ws,
                                                         unsigned* __restrict__ counters, int M,
-                                                        int N, int K, int nbs, int xs_m,
-                                                        int ss_m) {
+                                                        int N, int K, int nbs, int wsplit,
+                                                        int xs_m, int ss_m) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int nb = K / kBlockWeights;
-  const int slice = (int)blockIdx.y;
-  const int kb0 = slice * nbs;
-  const int nbw = min(nbs, nb - kb0);
   const int waves = (int)blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform per wave
   const int lane = (int)threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int tile_step = (int)gridDim.x * waves;
-  const int first = (int)blockIdx.x * waves + wave;
-  const int nstages = (nbw + kStageBlocks - 1) / kStageBlocks;
-  const int total = first < ntiles ? ((ntiles - 1 - first) / tile_step + 1) * nstages : 0;
+  const Split c = make_split(wave, waves, wsplit, nbs, nb, ntiles);
+  const int tile_step = (int)gridDim.x * c.T;
+  const int nstages = (c.nbw + kStageBlocks - 1) / kStageBlocks;
   const size_t row_bytes = (size_t)nb * kBlockBytes;
-  const uint8_t* slice_base = W + (size_t)kb0 * kBlockBytes;
+  const uint8_t* slice_base = W + (size_t)c.kb0 * kBlockBytes;
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
-  const uint32_t wbuf = (uint32_t)(lds_wbuf_base(M, xs_m, ss_m) + wave * 16 * kBufRowStride);
-  const StageArgs st{x, M, K, kb0, nbw, xs_m, ss_m, lds_x, lds_s};
+  const int red_base = lds_red_base(M, xs_m, ss_m);
+  float* red = reinterpret_cast<float*>(lds + red_base);
+  const uint32_t wbuf =
+      (uint32_t)(red_base + lds_red_bytes(M, waves, wsplit) + wave * 16 * kBufRowStride);
+  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s};
   const float rcp = 1.0f / (float)M;
   StageBatch sb;
   const int last_base = tstage_lead(st, rcp, sb);
   issue_barrier();
+  int tile = (int)blockIdx.x * c.T + c.wtile;
   StageLane sl;
-  stage_lane(lane, nb, 16, wbuf, sl);
-  StageRegs sr[R];
-  StreamPos ld{first, 0, total - 1};
-  if (total > 0) {
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
-                   sr[u]);
+  StageRegs sr;
+  if (tile < ntiles && nstages > 0) {
+    stage_lane(lane, nb, min(16, N - tile * 16), wbuf, sl);
+    stage_load(slice_base + (size_t)tile * 16 * row_bytes, sl, 0, c.nbw, sr);
   }
   tstage_finish(st, last_base, sb);
   __syncthreads();
@@ -795,131 +854,110 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
     sa[mt] = lds_s + 2 * (g * M + m);
   }
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
-  const int splits = (int)gridDim.y;
-  const size_t mn = (size_t)M * (size_t)N;
-  int tile = first, cs = 0;
+  constexpr int NV = 4 * MT;  // rows m = 16 mt + 4 g + i of this lane's outputs
+  int mrow[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int m = 16 * (k >> 2) + 4 * g + (k & 3);
+    mrow[k] = min(m, M - 1);
+    ok[k] = m < M;
+  }
+  const int ns = max(nstages, 1);
+  const int total = c.iters * ns;
+  int cs = 0, it = 0;
   f4_t acc[MT];
-  for (int t = 0; t < total; t += R) {
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      stage_store(lds, sl, sr[u]);
-      stream_issue<R>(slice_base, row_bytes, N, nb, nbw, nstages, tile_step, lane, wbuf, sl, ld,
-                   sr[u]);
-      if (t + u < total) {
-        if (cs == 0) {
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < total; ++e) {
+    const bool valid = tile < ntiles;
+    if (valid && nstages > 0) {
+      stage_store(lds, sl, sr);
+      int nt = tile, nsn = cs + 1;
+      if (nsn == nstages) {
+        nsn = 0;
+        nt += tile_step;
+      }
+      if (nt < ntiles) {
+        if (nsn == 0 && N - nt * 16 < 16) stage_lane(lane, nb, N - nt * 16, wbuf, sl);
+        stage_load(slice_base + (size_t)nt * 16 * row_bytes, sl, nsn, c.nbw, sr);
+      }
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
-        }
-// block j+1's LDS reads are issued before block j is computed (the buffer
-        // holds the whole stage; past the slice end they read unused chunks)
-        BlockRegs br[2];
-        read_block(rowbuf, g, 0, br[0]);
-#pragma unroll
-        for (int j = 0; j < kStageBlocks; ++j) {
-          const int bl = cs * kStageBlocks + j;
-          if (j + 1 < kStageBlocks) read_block(rowbuf, g, j + 1, br[(j + 1) & 1]);
-          if (bl < nbw) tiled_block<MT>(br[j & 1], hl, xa, sa, bl, M, acc);
-        }
-        if (++cs == nstages) {
-          const int n = tile * 16 + r;
-          if (splits == 1) {
-            if (n < N) {
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int m = 16 * mt + 4 * g + i;
-                  if (m < M) y[(size_t)m * N + n] = acc[mt][i];
-                }
-            }
-          } else {
-            if (n < N) {
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int m = 16 * mt + 4 * g + i;
-                  if (m < M) store_partial(ws + (size_t)slice * mn + (size_t)m * N + n, acc[mt][i]);
-                }
-            }
-            if (arrive_last(counters + tile, splits, lane) && n < N) {
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int m = 16 * mt + 4 * g + i;
-                  if (m < M)
-                    y[(size_t)m * N + n] =
-                        sum_slices(ws, mn, splits, slice, acc[mt][i], (size_t)m * N + n);
-                }
-            }
-          }
-          cs = 0;
-          tile += tile_step;
+      for (int j = 0; j < kStageBlocks; ++j) {
+        const int bl = cs * kStageBlocks + j;
+        if (bl < c.nbw) {
+          BlockRegs br;
+          read_block(rowbuf, g, j, br);
+          tiled_block<MT>(br, hl, xa, sa, c.bl_off + bl, M, acc);
         }
       }
+    }
+    if (++cs == ns) {
+      float v[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[k] = acc[k >> 2][k & 3];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+      finish_tile<NV>(v, mrow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, tile, y, ws,
+                      counters, lane);
+      cs = 0;
+      ++it;
+      tile += tile_step;
     }
   }
 }
 
-// Entry points: [ring depth - 1][rows - 1] for the row-vector kernel,
-// [ring depth - 1][MFMA row tiles - 1] for the tiled kernel.
-#define QMM_V(m, r) reinterpret_cast<const void*>(&qmm_vector_kernel<m, r>)
-#define QMM_V8(b, r) QMM_V(b + 1, r), QMM_V(b + 2, r), QMM_V(b + 3, r), QMM_V(b + 4, r), \
-                     QMM_V(b + 5, r), QMM_V(b + 6, r), QMM_V(b + 7, r), QMM_V(b + 8, r)
-const void* const kVectorFn[kMaxRing][32] = {
-    {QMM_V8(0, 1), QMM_V8(8, 1), QMM_V8(16, 1), QMM_V8(24, 1)},
-    {QMM_V8(0, 2), QMM_V8(8, 2), QMM_V8(16, 2), QMM_V8(24, 2)}};
+// Entry points: [rows - 1] for the row-vector kernel, [MFMA row tiles - 1]
+// for the tiled kernel.
+#define QMM_V(m) reinterpret_cast<const void*>(&qmm_vector_kernel<m>)
+#define QMM_V8(b) QMM_V(b + 1), QMM_V(b + 2), QMM_V(b + 3), QMM_V(b + 4), \
+                  QMM_V(b + 5), QMM_V(b + 6), QMM_V(b + 7), QMM_V(b + 8)
+const void* const kVectorFn[32] = {QMM_V8(0), QMM_V8(8), QMM_V8(16), QMM_V8(24)};
 #undef QMM_V8
 #undef QMM_V
-const void* const kTiledFn[kMaxRing][2] = {
-    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, 1>),
-     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, 1>)},
-    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, 2>),
-     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, 2>)}};
+const void* const kTiledFn[2] = {reinterpret_cast<const void*>(&qmm_tiled_kernel<1>),
+                                 reinterpret_cast<const void*>(&qmm_tiled_kernel<2>)};
 
-const void* kernel_fn(int kernel, int M, int ring) {
-  if (ring < 1 || ring > kMaxRing || M < 1 || M > 32) return nullptr;
-  return kernel == 2 ? kTiledFn[ring - 1][M > 16 ? 1 : 0] : kVectorFn[ring - 1][M - 1];
+const void* kernel_fn(int kernel, int M) {
+  if (M < 1 || M > 32) return nullptr;
+  return kernel == 2 ? kTiledFn[M > 16 ? 1 : 0] : kVectorFn[M - 1];
 }
 
 }  // namespace
 
 hipError_t prepare_kernels() {
-  for (int r = 0; r < kMaxRing; ++r) {
-    for (int m = 0; m < 32; ++m) {
-      hipError_t e = hipFuncSetAttribute(kVectorFn[r][m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
-      if (e != hipSuccess) return e;
-    }
-    for (int t = 0; t < 2; ++t) {
-      hipError_t e = hipFuncSetAttribute(kTiledFn[r][t], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
-      if (e != hipSuccess) return e;
-    }
+  for (int m = 0; m < 32; ++m) {
+    hipError_t e = hipFuncSetAttribute(kVectorFn[m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e != hipSuccess) return e;
+  }
+  for (int t = 0; t < 2; ++t) {
+    hipError_t e = hipFuncSetAttribute(kTiledFn[t], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t resident_per_cu(int kernel, int M, int ring, int waves, int lds_bytes, int* out) {
-  const void* f = kernel_fn(kernel, M, ring);
+hipError_t resident_per_cu(int kernel, int M, int waves, int lds_bytes, int* out) {
+  const void* f = kernel_fn(kernel, M);
   if (!f) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64 * waves, (size_t)lds_bytes);
 }
 
 hipError_t launch(const Launch& a, hipStream_t stream) {
-  const void* f = kernel_fn(a.kernel, a.M, a.ring);
+  const void* f = kernel_fn(a.kernel, a.M);
   if (!f) return hipErrorInvalidValue;
-  const dim3 grid(a.grid_x, a.splits), block(64 * a.waves_per_wg);
+  const dim3 grid(a.grid_x, a.grid_y), block(64 * a.waves_per_wg);
   const uint8_t* W = static_cast<const uint8_t*>(a.W);
-  int M = a.M, N = a.N, K = a.K, nbs = a.nbs, xs_m = a.xs_m, ss_m = a.ss_m;
+  int M = a.M, N = a.N, K = a.K, nbs = a.nbs, wsplit = a.wsplit, xs_m = a.xs_m, ss_m = a.ss_m;
   const float* x = a.x;
   float* y = a.y;
   float* ws = a.ws;
   unsigned* counters = a.counters;
   if (a.kernel == 2) {
-    void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &xs_m, &ss_m};
+    void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &wsplit, &xs_m, &ss_m};
     return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
   }
-  void* args[] = {&x, &W, &y, &ws, &counters, &N, &K, &nbs, &xs_m, &ss_m};
+  void* args[] = {&x, &W, &y, &ws, &counters, &N, &K, &nbs, &wsplit, &xs_m, &ss_m};
   return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
 }
 

@@ -70,9 +70,12 @@ def test_plans_for_every_workload(planner):
         nb = K // 256
         assert 1 <= p["splits"] <= nb and p["blocks_per_split"] * p["splits"] >= nb
         assert p["blocks_per_split"] * (p["splits"] - 1) < nb  # no empty slice
-        assert p["workspace_bytes"] == (p["splits"] * M * N * 4 if p["splits"] > 1 else 0)
+        ws, wsp = p["waves_per_wg"], p["wave_splits"]
+        assert ws % wsp == 0 and p["splits"] >= wsp
+        ranges = -(-p["splits"] // wsp)
+        assert p["workspace_bytes"] == (ranges * M * N * 4 if ranges > 1 else 0)
         tiles = (N + 15) // 16
-        assert p["grid_x"] == -(-tiles // p["waves_per_wg"])
+        assert p["grid_x"] == -(-tiles // (ws // wsp))
 
 
 def test_switch_point_in_range(planner):
@@ -121,7 +124,7 @@ def test_overrides(planner):
     assert (p["waves_per_wg"], p["splits"], p["grid_x"]) == (4, 2, 40)
     sbb.qmm_set_shape(planner, 4, 2, 1)  # one workgroup walks all 128 tiles of a slice
     assert sbb.qmm_query_plan(planner, 4, 2048, 2048)["grid_x"] == 1
-    sbb.qmm_set_shape(planner, 3, 0, 0)
+    sbb.qmm_set_shape(planner, 9, 0, 0)  # at most 8 waves per workgroup
     with pytest.raises(sbb.QmmError):
         sbb.qmm_query_plan(planner, 4, 2048, 2048)
     sbb.qmm_set_shape(planner, 0, 9, 0)  # 9 slices of an 8-block K
@@ -130,9 +133,21 @@ def test_overrides(planner):
     sbb.qmm_set_shape(planner, 0, 0, 0)
     with pytest.raises(sbb.QmmError):
         sbb.qmm_set_kernel(planner, 7)
-    for ring in (1, 2):
-        sbb.qmm_set_ring(planner, ring)
-        assert sbb.qmm_query_plan(planner, 4, 2048, 2048)["ring"] == ring
+    # slices reduced inside a workgroup
+    sbb.qmm_set_shape(planner, 4, 4, 0)
+    sbb.qmm_set_wave_splits(planner, 2)
+    p = sbb.qmm_query_plan(planner, 4, 2048, 2048)
+    assert (p["wave_splits"], p["splits"]) == (2, 4) and p["workspace_bytes"] == 2 * 4 * 2048 * 4
+    sbb.qmm_set_wave_splits(planner, 4)
+    p = sbb.qmm_query_plan(planner, 4, 2048, 2048)
+    assert p["wave_splits"] == 4 and p["workspace_bytes"] == 0 and p["grid_x"] == 128
+    sbb.qmm_set_wave_splits(planner, 3)  # 4 waves are not a multiple of 3
     with pytest.raises(sbb.QmmError):
-        sbb.qmm_set_ring(planner, 3)
-    sbb.qmm_set_ring(planner, 0)
+        sbb.qmm_query_plan(planner, 4, 2048, 2048)
+    sbb.qmm_set_shape(planner, 6, 2, 0)  # fewer slices than wave splits
+    with pytest.raises(sbb.QmmError):
+        sbb.qmm_query_plan(planner, 4, 2048, 2048)
+    with pytest.raises(sbb.QmmError):
+        sbb.qmm_set_wave_splits(planner, 9)
+    sbb.qmm_set_wave_splits(planner, 0)
+    sbb.qmm_set_shape(planner, 0, 0, 0)

@@ -37,11 +37,11 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run(h, x, W, N, K, kernel=sbb.KERNEL_AUTO, shape=(0, 0, 0), fill=np.nan, ring=0):
+def run(h, x, W, N, K, kernel=sbb.KERNEL_AUTO, shape=(0, 0, 0), fill=np.nan, wave_splits=0):
     M = x.shape[0]
     sbb.qmm_set_kernel(h, kernel)
     sbb.qmm_set_shape(h, *shape)
-    sbb.qmm_set_ring(h, ring)
+    sbb.qmm_set_wave_splits(h, wave_splits)
     try:
         xd, Wd = to_dev(x), to_dev(W.reshape(-1))
         y = torch.full((M, N), fill, dtype=torch.float32, device="cuda")
@@ -51,7 +51,7 @@ def run(h, x, W, N, K, kernel=sbb.KERNEL_AUTO, shape=(0, 0, 0), fill=np.nan, rin
     finally:
         sbb.qmm_set_kernel(h, sbb.KERNEL_AUTO)
         sbb.qmm_set_shape(h, 0, 0, 0)
-        sbb.qmm_set_ring(h, 0)
+        sbb.qmm_set_wave_splits(h, 0)
 
 
 def check(y, yref, aref, what=""):
@@ -111,13 +111,42 @@ def test_small_tiled(h, M, N, K):
                                    (1, 1, 1), (2, 3, 5), (4, 1, 3), (8, 2, 1), (4, 10, 2)])
 @pytest.mark.parametrize("M,kernel", [(5, sbb.KERNEL_VECTOR), (12, sbb.KERNEL_TILED),
                                       (12, sbb.KERNEL_VECTOR), (3, sbb.KERNEL_TILED)])
-@pytest.mark.parametrize("ring", [1, 2])
-def test_launch_shapes(h, M, kernel, shape, ring):
+def test_launch_shapes(h, M, kernel, shape):
     N, K = 1000, 2560
     x, W = inputs(M, N, K, tag=31 + M)
-    y = run(h, x, W, N, K, kernel=kernel, shape=shape, ring=ring)
+    y = run(h, x, W, N, K, kernel=kernel, shape=shape)
     yref, aref = oracle.qmm(x, W, N, K)
-    check(y, yref, aref, "M=%d kernel=%d shape=%s ring=%d" % (M, kernel, shape, ring))
+    check(y, yref, aref, "M=%d kernel=%d shape=%s" % (M, kernel, shape))
+
+
+# K slices reduced inside a workgroup (in LDS), alone and combined with split-K
+# across workgroups, with persistent grids and with waves whose slice lies past
+# the end of K (10 super-blocks here)
+@pytest.mark.parametrize("shape,wsplit", [((2, 2, 0), 2), ((4, 4, 0), 4), ((5, 5, 0), 5),
+                                          ((4, 8, 0), 4), ((8, 4, 0), 4), ((6, 3, 0), 3),
+                                          ((8, 8, 3), 2), ((4, 10, 1), 2), ((3, 3, 2), 3),
+                                          ((8, 10, 0), 8), ((7, 7, 0), 7)])
+@pytest.mark.parametrize("M,kernel", [(1, sbb.KERNEL_VECTOR), (5, sbb.KERNEL_VECTOR),
+                                      (3, sbb.KERNEL_TILED), (12, sbb.KERNEL_TILED),
+                                      (20, sbb.KERNEL_TILED)])
+def test_wave_splits(h, M, kernel, shape, wsplit):
+    N, K = 1000, 2560
+    sbb.qmm_set_kernel(h, kernel)
+    sbb.qmm_set_shape(h, *shape)
+    sbb.qmm_set_wave_splits(h, wsplit)
+    try:
+        sbb.qmm_query_plan(h, M, N, K)
+    except sbb.QmmError as e:
+        assert e.status == sbb.QMM_ERR_INVALID_ARG
+        pytest.skip("this launch shape does not fit the LDS at M=%d" % M)
+    finally:
+        sbb.qmm_set_kernel(h, sbb.KERNEL_AUTO)
+        sbb.qmm_set_shape(h, 0, 0, 0)
+        sbb.qmm_set_wave_splits(h, 0)
+    x, W = inputs(M, N, K, tag=47 + M)
+    y = run(h, x, W, N, K, kernel=kernel, shape=shape, wave_splits=wsplit)
+    yref, aref = oracle.qmm(x, W, N, K)
+    check(y, yref, aref, "M=%d kernel=%d shape=%s wave_splits=%d" % (M, kernel, shape, wsplit))
 
 
 # ------------------------------------------------------------ the workloads
@@ -293,7 +322,7 @@ def test_errors_launch_nothing(h):
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), 33, N, K, s) == sbb.QMM_ERR_SHAPE
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), M, N, 300, s) == sbb.QMM_ERR_SHAPE
     assert raw(h, xd.data_ptr(), Wd.data_ptr(), xd.data_ptr() + 64, M, N, K, s) == sbb.QMM_ERR_OVERLAP
-    sbb.qmm_set_shape(h, 3, 0, 0)  # 3 waves per workgroup is not a launch shape
+    sbb.qmm_set_shape(h, 9, 0, 0)  # 9 waves per workgroup is not a launch shape
     try:
         assert raw(h, xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), M, N, K, s) == sbb.QMM_ERR_INVALID_ARG
     finally:
