@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--mode", default="pass", choices=["pass", "configs", "kernels", "copy"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ids", action="store_true", help="skip the expert-indexed record")
     ap.add_argument("--no-eager", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="one allocation per matrix instead of one weight arena")
@@ -263,6 +264,74 @@ def cpu_baseline(budget_s):
                       % ("/".join(str(rows_used[m]) for m in (1, 4, 8, 16)), total_s, oracle.threads())}
 
 
+def ids_measure(torch, sbb, synth, acc, h, reps=5):
+    """Expert-indexed product on gate+up-shaped experts (E = 8, 100 MB each):
+    rows spread over distinct experts, each distinct expert streamed once per
+    call. Weight bytes = distinct experts x matrix bytes; graph-replayed
+    sequences over all experts keep the weights cold. The same bytes through
+    one plain call per distinct expert are timed for comparison."""
+    import numpy as np
+    E, N, K = 8, 34816, 5120
+    mb = acc.weight_bytes(N, K)
+    dev = torch.device("cuda:0")
+    W = torch.empty(E * mb, dtype=torch.uint8, device=dev)
+    host = np.empty(mb, dtype=np.uint8)
+    for e in range(E):
+        synth.weights(N, K, tensor=90000 + e, seed=SEED, out=host.reshape(N, -1))
+        W[e * mb:(e + 1) * mb].copy_(torch.from_numpy(host))
+    lib = sbb.load()
+    out = {}
+    stream = torch.cuda.current_stream()
+    for M, ids in ((4, [0, 2, 4, 6]), (8, list(range(8))), (16, [m % 8 for m in range(16)])):
+        x = torch.from_numpy(synth.acts(M, K, tensor=91000 + M, seed=SEED)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        idd = torch.tensor(ids, dtype=torch.int32, device=dev)
+        distinct = sorted(set(ids))
+        groups = [(e, [m for m in range(M) if ids[m] == e]) for e in distinct]
+        xs = [(e, x[rows].contiguous(), torch.empty((len(rows), N), dtype=torch.float32, device=dev))
+              for e, rows in groups]
+
+        def run_ids(sp):
+            rc = lib.qmm_run_ids(h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(W.data_ptr()),
+                                 ctypes.c_void_p(idd.data_ptr()), E, ctypes.c_void_p(y.data_ptr()),
+                                 M, N, K, sp)
+            if rc:
+                raise RuntimeError(sbb.qmm_status_string(rc))
+
+        def run_plain(sp):
+            for e, xe, ye in xs:
+                rc = lib.qmm_run(h, ctypes.c_void_p(xe.data_ptr()),
+                                 ctypes.c_void_p(W.data_ptr() + e * mb), ctypes.c_void_p(ye.data_ptr()),
+                                 xe.shape[0], N, K, sp)
+                if rc:
+                    raise RuntimeError(sbb.qmm_status_string(rc))
+
+        res = {}
+        for name, fn in (("ids", run_ids), ("plain_per_expert", run_plain)):
+            fn(ctypes.c_void_p(stream.cuda_stream))
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / reps * 1e-3
+            acc.check_roofline(len(distinct) * mb, t, what="ids %s M=%d" % (name, M))
+            res[name] = {"us_per_call": round(t * 1e6, 2),
+                         "weight_gbs": round(acc.gbs(len(distinct) * mb, t), 1)}
+        out[str(M)] = {"distinct_experts": len(distinct), "weight_bytes": len(distinct) * mb, **res}
+    del W
+    torch.cuda.empty_cache()
+    return {"workload": "expert-indexed product, E=8 experts of 34816x5120 (gate+up shape), "
+                        "rows over distinct experts", "per_m": out}
+
+
 def mode_pass(args, torch, sbb, synth, acc):
     ms = [int(v) for v in args.ms.split(",")]
     P = Pass(torch, sbb, synth, acc, ms, args.layers, arena=not args.separate)
@@ -299,6 +368,9 @@ def mode_pass(args, torch, sbb, synth, acc):
     out["kernels"] = {s: {"launches": v["launches"], "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
                           "share": round(v["ms"] / sum(w["ms"] for w in sym.values()), 4)}
                       for s, v in sorted(sym.items())}
+    if not args.no_ids:
+        log("expert-indexed product...")
+        out["ids"] = ids_measure(torch, sbb, synth, acc, P.h)
     value = acc.gbs(P.weight_bytes * len(ms), ms_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -98,6 +98,22 @@ int qmm_create(qmm_handle* out, int device);
 int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y,
             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* Expert-indexed product (the MUL_MAT_ID case of the op test that the
+ * launch-shape patch passes, "sixi-asi 0.9", section "The patch"):
+ *
+ *   y[m,:] = x[m,:] . dequant(W_experts[ids[m]])^T   for every row m,
+ *
+ * W_experts holds E matrices of N x K in the layout above, consecutively
+ * (matrix e starts at byte e * qmm_weight_bytes(N, K)); ids is a device array of
+ * M int32 expert indices. Rows that use the same expert share one pass over
+ * its weights (each distinct expert is streamed once); rows whose id is
+ * outside [0, E) are not written (y keeps their previous contents).
+ *   x, y, M, N, K: as for qmm_run (ids 4-byte aligned, must not overlap y).
+ * Enqueued on `stream`; never synchronizes. Always uses the tiled kernel.
+ * Same status codes as qmm_run (E < 1 or a null ids: QMM_ERR_INVALID_ARG). */
+int qmm_run_ids(qmm_handle h, const float* x, const void* W_experts, const int32_t* ids,
+                int64_t E, float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* Free the handle and its workspace. qmm_destroy(NULL) is a no-op returning
  * QMM_OK. The caller must make sure no work enqueued with the handle is still
  * running. */

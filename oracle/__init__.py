@@ -129,3 +129,29 @@ def qmm(x, W, N, K, nthreads=0):
 
 def threads():
     return int(_load().oracle_threads())
+
+
+def qmm_ids(x, W_experts, ids, E, N, K, nthreads=0):
+    """Expert-indexed product: y[m] = x[m] . dequant(W_experts[ids[m]])^T, in binary64.
+
+    W_experts holds E packed N x K matrices back to back. Returns (y, a, written):
+    rows whose id lies outside [0, E) are not written (y and a are NaN there and
+    written[m] is False). This is the definition row group by row group: each
+    distinct expert's rows go through qmm_rows with that expert's matrix.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    W_experts = _u8(W_experts)
+    ids = np.asarray(ids, dtype=np.int64)
+    M = x.shape[0]
+    mb = int(N) * (int(K) // 256) * 144
+    if W_experts.size != int(E) * mb or ids.shape != (M,):
+        raise ValueError("shape mismatch")
+    y = np.full((M, int(N)), np.nan)
+    a = np.full((M, int(N)), np.nan)
+    written = (ids >= 0) & (ids < int(E))
+    for e in sorted(set(int(v) for v in ids[written])):
+        rows = np.nonzero(ids == e)[0]
+        ye, ae = qmm(x[rows], W_experts[e * mb:(e + 1) * mb], N, K, nthreads)
+        y[rows] = ye
+        a[rows] = ae
+    return y, a, written

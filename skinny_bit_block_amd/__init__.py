@@ -28,7 +28,7 @@ QMM_DEVICE_NONE = -1  # planning-only handle: plans and checks arguments, never 
 KERNEL_AUTO, KERNEL_VECTOR, KERNEL_TILED = 0, 1, 2
 KERNEL_NAMES = {KERNEL_VECTOR: "vector", KERNEL_TILED: "tiled"}
 
-EXPORTS = ["qmm_create", "qmm_run", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
+EXPORTS = ["qmm_create", "qmm_run", "qmm_run_ids", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
            "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_wave_splits",
            "qmm_switch_point"]
 
@@ -59,6 +59,8 @@ def load():
         lib.qmm_create.restype = ctypes.c_int
         lib.qmm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         lib.qmm_run.restype = ctypes.c_int
+        lib.qmm_run_ids.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, i64, vp]
+        lib.qmm_run_ids.restype = ctypes.c_int
         lib.qmm_destroy.argtypes = [vp]
         lib.qmm_destroy.restype = ctypes.c_int
         lib.qmm_status_string.argtypes = [ctypes.c_int]
@@ -149,6 +151,40 @@ def qmm_run(h, x, W_blocks, y, M, N, K, stream=None):
         raise ValueError("W_blocks has fewer than N*K/256*144 bytes")
     return _check(load().qmm_run(h, _ptr(x), _ptr(W_blocks), _ptr(y), int(M), int(N), int(K),
                                  _stream(stream)))
+
+
+def qmm_run_ids(h, x, W_experts, ids, E, y, M, N, K, stream=None):
+    """Enqueue y[m] = x[m] . dequant(W_experts[ids[m]])^T on `stream`.
+
+    W_experts: uint8 device tensor of E matrices of N*K/256*144 bytes each;
+    ids: int32 device tensor of M expert indices (rows with an id outside [0, E)
+    are not written). Other arguments as for qmm_run.
+    """
+    for name, t, dt in (("x", x, "float32"), ("W_experts", W_experts, "uint8"),
+                        ("ids", ids, "int32"), ("y", y, "float32")):
+        if t is not None and not isinstance(t, int):
+            if not t.is_cuda:
+                raise ValueError("%s must be a device tensor" % name)
+            if str(t.dtype) != "torch." + dt:
+                raise ValueError("%s must be %s" % (name, dt))
+            if not t.is_contiguous():
+                raise ValueError("%s must be contiguous" % name)
+    if x is not None and not isinstance(x, int) and x.numel() < M * K:
+        raise ValueError("x has fewer than M*K elements")
+    if y is not None and not isinstance(y, int) and y.numel() < M * N:
+        raise ValueError("y has fewer than M*N elements")
+    if ids is not None and not isinstance(ids, int) and ids.numel() < M:
+        raise ValueError("ids has fewer than M elements")
+    if W_experts is not None and not isinstance(W_experts, int) and \
+            W_experts.numel() < qmm_weight_bytes(N, K) * E:
+        raise ValueError("W_experts has fewer than E*N*K/256*144 bytes")
+    return _check(load().qmm_run_ids(h, _ptr(x), _ptr(W_experts), _ptr(ids), int(E), _ptr(y),
+                                     int(M), int(N), int(K), _stream(stream)))
+
+
+def qmm_run_ids_raw(h, x_ptr, w_ptr, ids_ptr, E, y_ptr, M, N, K, stream_ptr):
+    """The C call with raw pointers; returns the status instead of raising."""
+    return load().qmm_run_ids(h, x_ptr, w_ptr, ids_ptr, E, y_ptr, M, N, K, stream_ptr)
 
 
 def qmm_run_raw(h, x_ptr, w_ptr, y_ptr, M, N, K, stream_ptr):

@@ -123,7 +123,9 @@ int64_t resident(qmm_ctx* h, int kernel, int M, int waves, int lds) {
   return (int64_t)wgs * h->cus;
 }
 
-int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
+// slots > 0: an expert-indexed call (tiled kernel only), whose grid holds up
+// to `slots` independent row groups; 0 for a plain call.
+int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slots = 0) {
   int rc = check_shape(M, N, K);
   if (rc) return rc;
   const int nb = (int)(K / 256);
@@ -132,6 +134,12 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   int kernel = M >= table_switch(N, K) ? QMM_KERNEL_TILED : QMM_KERNEL_VECTOR;
   if (te) kernel = te->kernel;
   if (h->forced_kernel != QMM_KERNEL_AUTO) kernel = h->forced_kernel;
+  if (slots > 0) {
+    if (h->forced_kernel == QMM_KERNEL_VECTOR) return QMM_ERR_INVALID_ARG;
+    kernel = QMM_KERNEL_TILED;
+    te = nullptr;  // table entries are for plain calls
+  }
+  const int groups_in_grid = slots > 0 ? slots : 1;
 
   const int waves = h->force_waves ? h->force_waves
                                    : (te ? te->waves : (ntiles >= 4096 ? 8 : kDefaultWaves));
@@ -170,7 +178,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   if (lds > qmm::kLdsMax) return QMM_ERR_INVALID_ARG;
   const int64_t ws = grid_y > 1 ? (int64_t)grid_y * M * N * 4 : 0;
   if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
-  if (grid_y > 1 && ntiles > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
+  if (grid_y > 1 && ntiles * groups_in_grid > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
 
   // at most one row tile per tile group of wsplit waves, and no more
   // workgroups than the device holds at once: the waves then walk several
@@ -178,9 +186,11 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p) {
   const int groups = waves / wsplit;
   const int64_t need = (ntiles + groups - 1) / groups;
   int64_t grid = need;
-  const int64_t res = resident(h, kernel, (int)M, waves, lds);
+  // (expert-indexed calls run their own instantiation of the tiled kernel)
+  const int64_t res = resident(h, slots > 0 ? 3 : kernel, (int)M, waves, lds);
   if (res > 0) {
-    const int64_t per_range = res / grid_y > 0 ? res / grid_y : 1;
+    const int64_t per_range =
+        res / ((int64_t)grid_y * groups_in_grid) > 0 ? res / ((int64_t)grid_y * groups_in_grid) : 1;
     if (per_range < grid) grid = per_range;
   }
   if (h->force_grid) grid = h->force_grid;
@@ -364,6 +374,55 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_
   a.y = y;
   a.ws = h->ws;
   a.counters = h->counters;
+  a.ids = nullptr;
+  a.E = 0;
+  a.expert_bytes = 0;
+  a.slots = 1;
+  return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+int qmm_run_ids(qmm_handle h, const float* x, const void* W_experts, const int32_t* ids,
+                int64_t E, float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (!h || !x || !W_experts || !ids || !y || E < 1) return QMM_ERR_INVALID_ARG;
+  int rc = check_shape(M, N, K);
+  if (rc) return rc;
+  if (((uintptr_t)x & 15) || ((uintptr_t)W_experts & 15) || ((uintptr_t)y & 3) ||
+      ((uintptr_t)ids & 3))
+    return QMM_ERR_ALIGN;
+  const uint64_t expert_bytes = qmm_weight_bytes(N, K);
+  if ((uint64_t)E > (UINT64_MAX >> 1) / expert_bytes) return QMM_ERR_SHAPE;
+  const size_t ybytes = (size_t)(M * N * 4);
+  if (overlaps(y, ybytes, x, (size_t)(M * K * 4)) ||
+      overlaps(y, ybytes, W_experts, (size_t)(expert_bytes * (uint64_t)E)) ||
+      overlaps(y, ybytes, ids, (size_t)(M * 4)))
+    return QMM_ERR_OVERLAP;
+  const int slots = (int)(M < E ? M : E);
+  qmm_plan p;
+  rc = make_plan(h, M, N, K, &p, slots);
+  if (rc) return rc;
+  if (h->device < 0) return QMM_ERR_NO_DEVICE;
+  qmm::Launch a;
+  a.kernel = 3;  // the tiled kernel's expert-indexed instantiation
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.waves_per_wg = p.waves_per_wg;
+  a.wsplit = p.wave_splits;
+  a.grid_x = p.grid_x;
+  a.grid_y = (p.splits + p.wave_splits - 1) / p.wave_splits;
+  a.nbs = p.blocks_per_split;
+  a.xs_m = qmm::lds_xs_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.ss_m = qmm::lds_ss_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.lds_bytes = p.lds_bytes;
+  a.x = x;
+  a.W = W_experts;
+  a.y = y;
+  a.ws = h->ws;
+  a.counters = h->counters;
+  a.ids = ids;
+  a.E = (int)(E < 0x7FFFFFFF ? E : 0x7FFFFFFF);
+  a.expert_bytes = (long long)expert_bytes;
+  a.slots = slots;
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 

@@ -15,7 +15,7 @@ constexpr int kLdsMax = 160 * 1024;  // LDS a workgroup may allocate on gfx950
 constexpr int kMaxWavesPerWg = 8;
 
 struct Launch {
-  int kernel;       // 1 = row-vector, 2 = tiled (MFMA)
+  int kernel;       // 1 = row-vector, 2 = tiled (MFMA), 3 = tiled, expert-indexed
   int M, N, K;
   int waves_per_wg;
   int wsplit;       // K slices reduced inside one workgroup (waves_per_wg % wsplit == 0)
@@ -30,6 +30,12 @@ struct Launch {
   float* y;
   float* ws;        // split-K partials [grid_y][M][N] (grid_y > 1)
   unsigned* counters;  // split-K arrival counter per row tile, zero between calls
+  // expert-indexed calls (tiled kernel only): row m uses matrix ids[m] of E,
+  // expert_bytes apart; slots = grid.z = most distinct experts (1 otherwise)
+  const int* ids;
+  int E;
+  long long expert_bytes;
+  int slots;
 };
 
 // Row tiles a split-K call may have (one arrival counter each).

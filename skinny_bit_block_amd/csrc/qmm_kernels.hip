@@ -154,7 +154,14 @@ struct StageArgs {
   int M, K, kb0, nbw, xs_m, ss_m;
   char* lds_x;
   float* lds_s;
+  int rowreg;  // with an expert map: lane k holds the x row of local row k
+  bool remap;
 };
+
+// x row of local row m (the caller's own row unless rows are gathered)
+__device__ __forceinline__ int x_row(const StageArgs& a, int m) {
+  return a.remap ? __shfl(a.rowreg, m) : m;
+}
 
 __device__ __forceinline__ void stage_issue(const StageArgs& a, int base, StageBatch& b) {
   const int nunits = a.M * a.nbw * 32;
@@ -407,12 +414,13 @@ __device__ __forceinline__ float* red_slot(float* red, int par, const Split& c, 
   return red + (size_t)(((par * c.T + c.wtile) * wsplit + slice) * M) * 16;
 }
 
-// Output of one row tile: NV values per lane, for rows mrow[k] (ok[k]: row < M)
-// of output column n. Writes y, or with split-K across workgroups the partial
-// and, for the last slice to arrive, the sum of all slices in slice order.
+// Output of one row tile: NV values per lane, for output rows grow[k] (ok[k]:
+// the row exists) of output column n. Writes y, or with split-K across
+// workgroups the partial and, for the last slice to arrive, the sum of all
+// slices in slice order. Mtot rows of y, counter ctr of the tile.
 template <int NV>
-__device__ __forceinline__ void write_tile(const float (&v)[NV], const int (&mrow)[NV],
-                                           const bool (&ok)[NV], int n, int N, int M, int tile,
+__device__ __forceinline__ void write_tile(const float (&v)[NV], const int (&grow)[NV],
+                                           const bool (&ok)[NV], int n, int N, int Mtot, int ctr,
                                            float* __restrict__ y, float* __restrict__ ws,
                                            unsigned* __restrict__ counters, int lane) {
   const int gsplits = (int)gridDim.y, gslice = (int)blockIdx.y;
@@ -420,37 +428,39 @@ __device__ __forceinline__ void write_tile(const float (&v)[NV], const int (&mro
     if (n < N) {
 #pragma unroll
       for (int k = 0; k < NV; ++k)
-        if (ok[k]) y[(size_t)mrow[k] * N + n] = v[k];
+        if (ok[k]) y[(size_t)grow[k] * N + n] = v[k];
     }
     return;
   }
-  const size_t mn = (size_t)M * (size_t)N;
+  const size_t mn = (size_t)Mtot * (size_t)N;
   if (n < N) {
 #pragma unroll
     for (int k = 0; k < NV; ++k)
-      if (ok[k]) store_partial(ws + (size_t)gslice * mn + (size_t)mrow[k] * N + n, v[k]);
+      if (ok[k]) store_partial(ws + (size_t)gslice * mn + (size_t)grow[k] * N + n, v[k]);
   }
-  if (arrive_last(counters + tile, gsplits, lane) && n < N) {
+  if (arrive_last(counters + ctr, gsplits, lane) && n < N) {
 #pragma unroll
     for (int k = 0; k < NV; ++k)
       if (ok[k])
-        y[(size_t)mrow[k] * N + n] =
-            sum_slices(ws, mn, gsplits, gslice, v[k], (size_t)mrow[k] * N + n);
+        y[(size_t)grow[k] * N + n] =
+            sum_slices(ws, mn, gsplits, gslice, v[k], (size_t)grow[k] * N + n);
   }
 }
 
 // One tile iteration's end: with wsplit > 1 the slices' partials meet in LDS
-// and the tile group's first wave writes the tile. Every wave of the workgroup
-// calls this once per iteration (it contains the barrier).
+// (indexed by local row mrow) and the tile group's first wave writes the tile.
+// Every wave of the workgroup calls this once per iteration (it contains the
+// barrier).
 template <int NV>
 __device__ __forceinline__ void finish_tile(float (&v)[NV], const int (&mrow)[NV],
-                                            const bool (&ok)[NV], bool valid, int it,
-                                            const Split& c, int wsplit, float* red, int r,
-                                            int n, int N, int M, int tile, float* __restrict__ y,
+                                            const int (&grow)[NV], const bool (&ok)[NV],
+                                            bool valid, int it, const Split& c, int wsplit,
+                                            float* red, int r, int n, int N, int M, int Mtot,
+                                            int ctr, float* __restrict__ y,
                                             float* __restrict__ ws, unsigned* __restrict__ counters,
                                             int lane) {
   if (wsplit == 1) {
-    if (valid) write_tile<NV>(v, mrow, ok, n, N, M, tile, y, ws, counters, lane);
+    if (valid) write_tile<NV>(v, grow, ok, n, N, Mtot, ctr, y, ws, counters, lane);
     return;
   }
   const int par = it & 1;
@@ -469,7 +479,7 @@ __device__ __forceinline__ void finish_tile(float (&v)[NV], const int (&mrow)[NV
       for (int sl = 1; sl < wsplit; ++sl) sum += red_slot(red, par, c, wsplit, sl, M)[mrow[k] * 16 + r];
       v[k] = sum;
     }
-    write_tile<NV>(v, mrow, ok, n, N, M, tile, y, ws, counters, lane);
+    write_tile<NV>(v, grow, ok, n, N, Mtot, ctr, y, ws, counters, lane);
   }
 }
 
@@ -577,7 +587,7 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
   float* red = reinterpret_cast<float*>(lds + red_base);
   const uint32_t wbuf =
       (uint32_t)(red_base + lds_red_bytes(M, waves, wsplit) + wave * 16 * kBufRowStride);
-  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s};
+  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s, 0, false};
   StageBatch sb;
   stage_issue(st, 0, sb);
   issue_barrier();
@@ -649,8 +659,8 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
         if ((m & 3) == g) v[m >> 2] = t;
         acc[m] = 0.f;
       }
-      finish_tile<NV>(v, mrow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, tile, y, ws,
-                      counters, lane);
+      finish_tile<NV>(v, mrow, mrow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, M,
+                      tile, y, ws, counters, lane);
       cs = 0;
       ++it;
       tile += tile_step;
@@ -689,8 +699,8 @@ __device__ __forceinline__ void tstage_issue(const StageArgs& a, int base, float
   for (int i = 0; i < kStageBatch; ++i) {
     const int u = base + i * nthr + (int)threadIdx.x;
     const TUnit c = tunit(u < nunits ? u : 0, a.M, rcp);
-    const float* src =
-        a.x + (size_t)c.m * a.K + (size_t)(a.kb0 + c.bl) * kBlockWeights + 64 * c.g + 4 * c.t;
+    const float* src = a.x + (size_t)x_row(a, c.m) * a.K + (size_t)(a.kb0 + c.bl) * kBlockWeights +
+                       64 * c.g + 4 * c.t;
     b.lo[i] = *reinterpret_cast<const float4*>(src);
     b.hi[i] = *reinterpret_cast<const float4*>(src + 32);
   }
@@ -796,14 +806,64 @@ __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLan
   }
 }
 
-template <int MT>
+// Expert-indexed calls (ids != nullptr): row m multiplies expert ids[m] of E
+// consecutive matrices (expert_bytes apart). grid.z enumerates the distinct
+// experts in ascending order; the workgroups of slot z stream that expert's
+// matrix once for all rows that use it (M of them, gathered through a lane
+// register map) and scatter the results. Rows whose id is outside [0, E) are
+// not written. Without ids, slot 0 is the whole call.
+struct Slot {
+  int M;           // rows of this slot
+  int rowreg;      // lane k: the caller's row of local row k
+  bool remap;
+  const uint8_t* W;
+  int ctr_base;    // first split-K counter of this slot
+  bool empty;      // no expert for this slot
+};
+
+__device__ __forceinline__ Slot make_slot(const int* __restrict__ ids, int E, long long expert_bytes,
+                                          const uint8_t* W, int Mtot, int ntiles, int lane) {
+  Slot o{Mtot, lane, false, W, 0, false};
+  if (!ids) return o;
+  const int id = lane < Mtot ? ids[lane] : -1;
+  const bool valid = id >= 0 && id < E;
+  bool first = valid;  // no earlier row has the same id
+  for (int j = 0; j < Mtot; ++j) {
+    const int oj = __shfl(id, j);
+    if (j < lane && oj == id) first = false;
+  }
+  const unsigned long long fmask = __ballot(first);
+  int rank = 0;  // distinct valid ids below this one
+  for (int j = 0; j < Mtot; ++j) {
+    const int oj = __shfl(id, j);
+    if (((fmask >> j) & 1ull) && oj < id) ++rank;
+  }
+  const unsigned long long pick = __ballot(first && rank == (int)blockIdx.z);
+  if (pick == 0ull) {
+    o.empty = true;
+    return o;
+  }
+  const int e = __shfl(id, (int)__builtin_ctzll(pick));
+  const unsigned long long match = __ballot(valid && id == e);
+  o.M = (int)__popcll(match);
+  for (int j = 0; j < Mtot; ++j)
+    if (((match >> j) & 1ull) && (int)__popcll(match & ((1ull << j) - 1ull)) == lane) o.rowreg = j;
+  o.remap = true;
+  o.W = W + (size_t)e * (size_t)expert_bytes;
+  o.ctr_base = (int)blockIdx.z * ntiles;
+  return o;
+}
+
+template <int MT, bool IDS>
 __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict__ x,
                                                         const uint8_t* __restrict__ W,
                                                         float* __restrict__ y,
                                                         float* __restrict__ ws,
-                                                        unsigned* __restrict__ counters, int M,
+                                                        unsigned* __restrict__ counters, int Mtot,
                                                         int N, int K, int nbs, int wsplit,
-                                                        int xs_m, int ss_m) {
+                                                        int xs_m, int ss_m,
+                                                        const int* __restrict__ ids, int E,
+                                                        long long expert_bytes) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int nb = K / kBlockWeights;
   const int waves = (int)blockDim.x >> 6;
@@ -811,19 +871,24 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   const int lane = (int)threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = (N + 15) >> 4;
+  const Slot sl0 = IDS ? make_slot(ids, E, expert_bytes, W, Mtot, ntiles, lane)
+                       : Slot{Mtot, lane, false, W, 0, false};
+  if (IDS && sl0.empty) return;  // the same for every wave of the workgroup
+  const int M = sl0.M;    // rows of this call (or of this expert)
   const Split c = make_split(wave, waves, wsplit, nbs, nb, ntiles);
   const int tile_step = (int)gridDim.x * c.T;
   const int nstages = (c.nbw + kStageBlocks - 1) / kStageBlocks;
   const size_t row_bytes = (size_t)nb * kBlockBytes;
-  const uint8_t* slice_base = W + (size_t)c.kb0 * kBlockBytes;
+  const uint8_t* slice_base = sl0.W + (size_t)c.kb0 * kBlockBytes;
 
+  // LDS regions are laid out for Mtot rows; this slot uses the first M
   char* lds_x = lds;
-  float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
-  const int red_base = lds_red_base(M, xs_m, ss_m);
+  float* lds_s = reinterpret_cast<float*>(lds + Mtot * xs_m);
+  const int red_base = lds_red_base(Mtot, xs_m, ss_m);
   float* red = reinterpret_cast<float*>(lds + red_base);
   const uint32_t wbuf =
-      (uint32_t)(red_base + lds_red_bytes(M, waves, wsplit) + wave * 16 * kBufRowStride);
-  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s};
+      (uint32_t)(red_base + lds_red_bytes(Mtot, waves, wsplit) + wave * 16 * kBufRowStride);
+  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s, sl0.rowreg, IDS};
   const float rcp = 1.0f / (float)M;
   StageBatch sb;
   const int last_base = tstage_lead(st, rcp, sb);
@@ -855,13 +920,14 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   }
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
   constexpr int NV = 4 * MT;  // rows m = 16 mt + 4 g + i of this lane's outputs
-  int mrow[NV];
+  int mrow[NV], grow[NV];
   bool ok[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int m = 16 * (k >> 2) + 4 * g + (k & 3);
     mrow[k] = min(m, M - 1);
     ok[k] = m < M;
+    grow[k] = IDS ? __shfl(sl0.rowreg, mrow[k]) : mrow[k];
   }
   const int ns = max(nstages, 1);
   const int total = c.iters * ns;
@@ -898,8 +964,8 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
       for (int k = 0; k < NV; ++k) v[k] = acc[k >> 2][k & 3];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
-      finish_tile<NV>(v, mrow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, tile, y, ws,
-                      counters, lane);
+      finish_tile<NV>(v, mrow, grow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, Mtot,
+                      sl0.ctr_base + tile, y, ws, counters, lane);
       cs = 0;
       ++it;
       tile += tile_step;
@@ -915,12 +981,18 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
 const void* const kVectorFn[32] = {QMM_V8(0), QMM_V8(8), QMM_V8(16), QMM_V8(24)};
 #undef QMM_V8
 #undef QMM_V
-const void* const kTiledFn[2] = {reinterpret_cast<const void*>(&qmm_tiled_kernel<1>),
-                                 reinterpret_cast<const void*>(&qmm_tiled_kernel<2>)};
+// [expert-indexed][row tiles - 1]
+const void* const kTiledFn[2][2] = {
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false>)},
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, true>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, true>)}};
 
 const void* kernel_fn(int kernel, int M) {
   if (M < 1 || M > 32) return nullptr;
-  return kernel == 2 ? kTiledFn[M > 16 ? 1 : 0] : kVectorFn[M - 1];
+  if (kernel == 1) return kVectorFn[M - 1];
+  if (kernel == 2 || kernel == 3) return kTiledFn[kernel == 3][M > 16 ? 1 : 0];
+  return nullptr;
 }
 
 }  // namespace
@@ -930,8 +1002,9 @@ hipError_t prepare_kernels() {
     hipError_t e = hipFuncSetAttribute(kVectorFn[m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
   }
-  for (int t = 0; t < 2; ++t) {
-    hipError_t e = hipFuncSetAttribute(kTiledFn[t], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+  for (int t = 0; t < 4; ++t) {
+    hipError_t e = hipFuncSetAttribute(kTiledFn[t >> 1][t & 1],
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -946,15 +1019,19 @@ hipError_t resident_per_cu(int kernel, int M, int waves, int lds_bytes, int* out
 hipError_t launch(const Launch& a, hipStream_t stream) {
   const void* f = kernel_fn(a.kernel, a.M);
   if (!f) return hipErrorInvalidValue;
-  const dim3 grid(a.grid_x, a.grid_y), block(64 * a.waves_per_wg);
+  const dim3 grid(a.grid_x, a.grid_y, a.slots), block(64 * a.waves_per_wg);
   const uint8_t* W = static_cast<const uint8_t*>(a.W);
   int M = a.M, N = a.N, K = a.K, nbs = a.nbs, wsplit = a.wsplit, xs_m = a.xs_m, ss_m = a.ss_m;
   const float* x = a.x;
   float* y = a.y;
   float* ws = a.ws;
   unsigned* counters = a.counters;
-  if (a.kernel == 2) {
-    void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &wsplit, &xs_m, &ss_m};
+  const int* ids = a.ids;
+  int E = a.E;
+  long long expert_bytes = a.expert_bytes;
+  if (a.kernel != 1) {
+    void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &wsplit, &xs_m, &ss_m,
+                    &ids, &E, &expert_bytes};
     return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
   }
   void* args[] = {&x, &W, &y, &ws, &counters, &N, &K, &nbs, &wsplit, &xs_m, &ss_m};

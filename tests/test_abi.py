@@ -151,3 +151,17 @@ def test_overrides(planner):
         sbb.qmm_set_wave_splits(planner, 9)
     sbb.qmm_set_wave_splits(planner, 0)
     sbb.qmm_set_shape(planner, 0, 0, 0)
+
+
+def test_run_ids_argument_checks(planner):
+    run = sbb.qmm_run_ids_raw
+    ok = (0x10000, 0x20000000, 0x30000000, 8, 0x40000000, 4, 16, 256, 0)
+    assert run(None, *ok) == sbb.QMM_ERR_INVALID_ARG
+    assert run(planner, 0x10000, 0x20000000, 0, 8, 0x40000000, 4, 16, 256, 0) == sbb.QMM_ERR_INVALID_ARG
+    assert run(planner, 0x10000, 0x20000000, 0x30000000, 0, 0x40000000, 4, 16, 256, 0) == sbb.QMM_ERR_INVALID_ARG
+    assert run(planner, 0x10000, 0x20000000, 0x30000002, 8, 0x40000000, 4, 16, 256, 0) == sbb.QMM_ERR_ALIGN
+    assert run(planner, 0x10000, 0x20000000, 0x30000000, 8, 0x40000000, 33, 16, 256, 0) == sbb.QMM_ERR_SHAPE
+    # y over the ids, over the last expert's bytes
+    assert run(planner, 0x10000, 0x20000000, 0x40000000 + 8, 8, 0x40000000, 4, 16, 256, 0) == sbb.QMM_ERR_OVERLAP
+    assert run(planner, 0x10000, 0x20000000, 0x30000000, 8, 0x20000000 + 7 * 16 * 144, 4, 16, 256, 0) == sbb.QMM_ERR_OVERLAP
+    assert run(planner, *ok) == sbb.QMM_ERR_NO_DEVICE
