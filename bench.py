@@ -146,7 +146,7 @@ class Pass:
     def kernel_symbol(self, M, N, K):
         p = self.plan(M, N, K)
         if p["kernel"] == self.sbb.KERNEL_TILED:
-            return "qmm_tiled_kernel<%d>" % (1 if M <= 16 else 2)
+            return "qmm_tiled_kernel<%d, false>" % (1 if M <= 16 else 2)
         return "qmm_vector_kernel<%d>" % M
 
 
