@@ -140,13 +140,20 @@ __device__ __forceinline__ Header decode_header(u4_t h, const HeaderLane& c) {
 // 32+4t+1, 32+4t+3}; sums[m][bl][j] is the fp32 sum of the rounded x over
 // sub-block j. The eight lanes t = 0..7 of a (m, bl, g) group are adjacent,
 // so the sub-block sums are a fixed xor-butterfly over those lanes.
-// A thread handles kStageBatch units per batch and issues all their loads
-// before it converts any; the first batch is issued before the weight ring,
-// so the latencies of x and of the first weights overlap.
-constexpr int kStageBatch = 4;
+// All x units of a workgroup are loaded at once when they fit in U units per
+// thread (U = kVectorLead or kTiledLead); a larger slice first stages chunks
+// of U units per thread one after another. The last chunk's loads are issued
+// before the first weight stage, and its conversion waits only for them (an
+// s_waitcnt that leaves the weight stage's kStageLoads loads outstanding), so
+// x and the first weights are in flight together. Every load of a chunk is
+// issued unconditionally (lanes past the end re-read the last unit), which
+// keeps the compiler's wait counts exact.
+constexpr int kVectorLead = 8;
+constexpr int kTiledLead = 16;
 
-struct StageBatch {
-  float4 lo[kStageBatch], hi[kStageBatch];
+template <int U>
+struct XRegs {
+  float4 lo[U], hi[U];
 };
 
 struct StageArgs {
@@ -163,19 +170,58 @@ __device__ __forceinline__ int x_row(const StageArgs& a, int m) {
   return a.remap ? __shfl(a.rowreg, m) : m;
 }
 
-__device__ __forceinline__ void stage_issue(const StageArgs& a, int base, StageBatch& b) {
-  const int nunits = a.M * a.nbw * 32;
+// q = u / d for u < 2^24 and 1 <= d <= 32: a float estimate is within one of
+// the quotient; one correction step makes it exact.
+__device__ __forceinline__ int div_small(int u, int d, float rcp) {
+  int q = (int)((float)u * rcp);
+  const int rem = u - q * d;
+  q += rem < 0 ? -1 : (rem >= d ? 1 : 0);
+  return q;
+}
+
+struct TUnit {
+  int m, g, t, bl;
+};
+
+// tiled order: u = ((bl*8 + t)*4 + g)*M + m
+__device__ __forceinline__ TUnit tunit(int u, int M, float rcp) {
+  const int rest = div_small(u, M, rcp);
+  return TUnit{u - rest * M, rest & 3, (rest >> 2) & 7, rest >> 5};
+}
+
+// First of the 8 fp32 values of unit u (the other four are 32 further on).
+// Row-vector order: u = ((m*nbw + bl)*4 + g)*8 + t.
+template <bool TILED>
+__device__ __forceinline__ const float* unit_src(const StageArgs& a, int u, float rcp) {
+  int m, g, t, bl;
+  if (TILED) {
+    const TUnit c = tunit(u, a.M, rcp);
+    m = x_row(a, c.m);
+    g = c.g;
+    t = c.t;
+    bl = c.bl;
+  } else {
+    t = u & 7;
+    g = (u >> 3) & 3;
+    const int rest = u >> 5;
+    bl = rest % a.nbw;
+    m = rest / a.nbw;
+  }
+  return a.x + (size_t)m * a.K + (size_t)(a.kb0 + bl) * kBlockWeights + 64 * g + 4 * t;
+}
+
+template <bool TILED, int U>
+__device__ __forceinline__ void x_issue(const StageArgs& a, int base, int nu, float rcp,
+                                        XRegs<U>& b) {
+  const int last = a.M * a.nbw * 32 - 1;
   const int nthr = (int)blockDim.x;
 #pragma unroll
-  for (int i = 0; i < kStageBatch; ++i) {
-    const int u = base + i * nthr + (int)threadIdx.x;
-    const int uu = u < nunits ? u : 0;
-    const int t = uu & 7, g = (uu >> 3) & 3, rest = uu >> 5;
-    const int bl = rest % a.nbw, m = rest / a.nbw;
-    const float* src =
-        a.x + (size_t)m * a.K + (size_t)(a.kb0 + bl) * kBlockWeights + 64 * g + 4 * t;
-    b.lo[i] = *reinterpret_cast<const float4*>(src);
-    b.hi[i] = *reinterpret_cast<const float4*>(src + 32);
+  for (int j = 0; j < U; ++j) {
+    if (j < nu) {  // uniform across the workgroup
+      const float* src = unit_src<TILED>(a, min(base + j * nthr + (int)threadIdx.x, last), rcp);
+      b.lo[j] = *reinterpret_cast<const float4*>(src);
+      b.hi[j] = *reinterpret_cast<const float4*>(src + 32);
+    }
   }
 }
 
@@ -188,59 +234,96 @@ __device__ __forceinline__ void stage_issue(const StageArgs& a, int base, StageB
 //     16*(((bl*8 + t)*4 + g)*M + m), the order the MFMA A operand reads, so
 //     the 16 lanes of a j-pair read M consecutive units (rows past M repeat
 //     real rows); sums of (m, bl, g) as a float2 at 8*((bl*4 + g)*M + m).
-__device__ __forceinline__ void stage_finish(const StageArgs& a, int base, const StageBatch& b) {
-  const int nunits = a.M * a.nbw * 32;
-  const int nthr = (int)blockDim.x;
-#pragma unroll
-  for (int i = 0; i < kStageBatch; ++i) {
-    if (base + i * nthr >= nunits) break;  // uniform across the workgroup
-    const int u = base + i * nthr + (int)threadIdx.x;
-    const bool ok = u < nunits;
-    const int uu = ok ? u : 0;
-    const int t = uu & 7, g = (uu >> 3) & 3, rest = uu >> 5;
-    const int bl = rest % a.nbw, m = rest / a.nbw;
-    const _Float16 l0 = (_Float16)b.lo[i].x, l1 = (_Float16)b.lo[i].y,
-                   l2 = (_Float16)b.lo[i].z, l3 = (_Float16)b.lo[i].w;
-    const _Float16 h0 = (_Float16)b.hi[i].x, h1 = (_Float16)b.hi[i].y,
-                   h2 = (_Float16)b.hi[i].z, h3 = (_Float16)b.hi[i].w;
-    u4_t v;
-    v.x = pack_h2(l0, l2);
-    v.y = pack_h2(l1, l3);
-    v.z = pack_h2(h0, h2);
-    v.w = pack_h2(h1, h3);
-    float slo = ((float)l0 + (float)l1) + ((float)l2 + (float)l3);
-    float shi = ((float)h0 + (float)h1) + ((float)h2 + (float)h3);
-    slo += __shfl_xor(slo, 1);
-    shi += __shfl_xor(shi, 1);
-    slo += __shfl_xor(slo, 2);
-    shi += __shfl_xor(shi, 2);
-    slo += __shfl_xor(slo, 4);
-    shi += __shfl_xor(shi, 4);
-    if (ok) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
-      const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
-      dst[p0] = v.x;
-      dst[p0 + 2] = v.y;
-      dst[p0 + 4] = v.z;
-      dst[p0 + 6] = v.w;
-      if (t == 0) {
-        a.lds_s[m * a.ss_m + bl * 8 + 2 * g] = slo;
-        a.lds_s[m * a.ss_m + bl * 8 + 2 * g + 1] = shi;
-      }
+__device__ __forceinline__ void vector_unit_store(const StageArgs& a, int u, bool ok,
+                                                  const float4& lo, const float4& hi) {
+  const int uu = ok ? u : 0;
+  const int t = uu & 7, g = (uu >> 3) & 3, rest = uu >> 5;
+  const int bl = rest % a.nbw, m = rest / a.nbw;
+  const _Float16 l0 = (_Float16)lo.x, l1 = (_Float16)lo.y, l2 = (_Float16)lo.z,
+                 l3 = (_Float16)lo.w;
+  const _Float16 h0 = (_Float16)hi.x, h1 = (_Float16)hi.y, h2 = (_Float16)hi.z,
+                 h3 = (_Float16)hi.w;
+  u4_t v;
+  v.x = pack_h2(l0, l2);
+  v.y = pack_h2(l1, l3);
+  v.z = pack_h2(h0, h2);
+  v.w = pack_h2(h1, h3);
+  float slo = ((float)l0 + (float)l1) + ((float)l2 + (float)l3);
+  float shi = ((float)h0 + (float)h1) + ((float)h2 + (float)h3);
+  slo += __shfl_xor(slo, 1);
+  shi += __shfl_xor(shi, 1);
+  slo += __shfl_xor(slo, 2);
+  shi += __shfl_xor(shi, 2);
+  slo += __shfl_xor(slo, 4);
+  shi += __shfl_xor(shi, 4);
+  if (ok) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
+    const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
+    dst[p0] = v.x;
+    dst[p0 + 2] = v.y;
+    dst[p0 + 4] = v.z;
+    dst[p0 + 6] = v.w;
+    if (t == 0) {
+      a.lds_s[m * a.ss_m + bl * 8 + 2 * g] = slo;
+      a.lds_s[m * a.ss_m + bl * 8 + 2 * g + 1] = shi;
     }
   }
 }
 
-// Batches after the first (only when a slice holds more than
-// kStageBatch units per thread).
-__device__ __forceinline__ void stage_rest(const StageArgs& a) {
-  const int nunits = a.M * a.nbw * 32;
-  const int step = (int)blockDim.x * kStageBatch;
-  for (int base = step; base < nunits; base += step) {
-    StageBatch b;
-    stage_issue(a, base, b);
-    stage_finish(a, base, b);
+// dwords of a unit: x at block offsets 64g + {4t, 4t+2 | 4t+1, 4t+3 |
+// 32+4t, 32+4t+2 | 32+4t+1, 32+4t+3}, the order of the B operand's nibbles
+__device__ __forceinline__ void tiled_unit_store(const StageArgs& a, int u, bool ok,
+                                                 const float4& lo, const float4& hi) {
+  if (ok) {
+    u4_t v;
+    v.x = pack_h2((_Float16)lo.x, (_Float16)lo.z);
+    v.y = pack_h2((_Float16)lo.y, (_Float16)lo.w);
+    v.z = pack_h2((_Float16)hi.x, (_Float16)hi.z);
+    v.w = pack_h2((_Float16)hi.y, (_Float16)hi.w);
+    *reinterpret_cast<u4_t*>(a.lds_x + 16 * u) = v;
   }
+}
+
+template <bool TILED, int U>
+__device__ __forceinline__ void x_finish(const StageArgs& a, int base, int nu,
+                                         const XRegs<U>& b) {
+  const int nunits = a.M * a.nbw * 32;
+  const int nthr = (int)blockDim.x;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    if (j < nu) {  // uniform
+      const int u = base + j * nthr + (int)threadIdx.x;
+      if (TILED)
+        tiled_unit_store(a, u, u < nunits, b.lo[j], b.hi[j]);
+      else
+        vector_unit_store(a, u, u < nunits, b.lo[j], b.hi[j]);
+    }
+  }
+}
+
+// Stages every chunk but the last and issues the last one's loads; returns
+// that chunk's first unit and sets nu to its units per thread.
+template <bool TILED, int U>
+__device__ __forceinline__ int x_lead(const StageArgs& a, float rcp, XRegs<U>& b, int& nu) {
+  const int nthr = (int)blockDim.x;
+  int left = (a.M * a.nbw * 32 + nthr - 1) / nthr;
+  int base = 0;
+  for (; left > U; left -= U, base += U * nthr) {
+    x_issue<TILED, U>(a, base, U, rcp, b);
+    x_finish<TILED, U>(a, base, U, b);
+  }
+  x_issue<TILED, U>(a, base, left, rcp, b);
+  nu = left;
+  return base;
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0, expcnt and lgkmcnt at their maxima, so
+// only vmcnt is waited for).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
 }
 
 struct Quants {
@@ -327,6 +410,20 @@ __device__ __forceinline__ void stage_load(const uint8_t* wave_base, const Stage
 __device__ __forceinline__ void stage_store(char* lds, const StageLane& c, const StageRegs& sr) {
 #pragma unroll
   for (int i = 0; i < kStageLoads; ++i) *reinterpret_cast<u4_t*>(lds + c.loff[i]) = sr.v[i];
+}
+
+// The first stage of a wave's first tile. A wave without one (no tile, or no
+// K work) loads a stage of the matrix's first rows instead, which it never
+// stores: every wave then has exactly kStageLoads loads outstanding after its
+// x loads, the count the prologue's s_waitcnt relies on.
+__device__ __forceinline__ void first_stage(const uint8_t* W, const uint8_t* slice_base, int tile,
+                                            int ntiles, int nstages, int nb, int N, int nbw,
+                                            size_t row_bytes, int lane, uint32_t wbuf,
+                                            StageLane& sl, StageRegs& sr) {
+  const bool real = tile < ntiles && nstages > 0;
+  const int t = real ? tile : 0;
+  stage_lane(lane, nb, min(16, N - t * 16), wbuf, sl);
+  stage_load(real ? slice_base + (size_t)t * 16 * row_bytes : W, sl, 0, real ? nbw : nb, sr);
 }
 
 // One super-block as lane (r, g) needs it: the header and its j-pair's quants.
@@ -588,18 +685,16 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
   const uint32_t wbuf =
       (uint32_t)(red_base + lds_red_bytes(M, waves, wsplit) + wave * 16 * kBufRowStride);
   const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s, 0, false};
-  StageBatch sb;
-  stage_issue(st, 0, sb);
+  XRegs<kVectorLead> xb;
+  int xnu;
+  const int xbase = x_lead<false, kVectorLead>(st, 0.f, xb, xnu);
   issue_barrier();
   int tile = (int)blockIdx.x * c.T + c.wtile;
   StageLane sl;
   StageRegs sr;
-  if (tile < ntiles && nstages > 0) {
-    stage_lane(lane, nb, min(16, N - tile * 16), wbuf, sl);
-    stage_load(slice_base + (size_t)tile * 16 * row_bytes, sl, 0, c.nbw, sr);
-  }
-  stage_finish(st, 0, sb);
-  stage_rest(st);
+  first_stage(W, slice_base, tile, ntiles, nstages, nb, N, c.nbw, row_bytes, lane, wbuf, sl, sr);
+  wait_vm<kStageLoads>();  // x complete; the first weight stage stays in flight
+  x_finish<false, kVectorLead>(st, xbase, xnu, xb);
   __syncthreads();
 
   const HeaderLane hl = header_lane(g);
@@ -672,75 +767,6 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
 // Staging of the tiled kernel's activations: unit u = ((bl*8 + t)*4 + g)*M + m
 // goes to LDS byte 16u, so consecutive threads write consecutive units. The
 // sub-block sums are a second pass over the staged binary16 values.
-
-// q = u / d for u < 2^24 and 1 <= d <= 32: a float estimate is within one of
-// the quotient; one correction step makes it exact.
-__device__ __forceinline__ int div_small(int u, int d, float rcp) {
-  int q = (int)((float)u * rcp);
-  const int rem = u - q * d;
-  q += rem < 0 ? -1 : (rem >= d ? 1 : 0);
-  return q;
-}
-
-struct TUnit {
-  int m, g, t, bl;
-};
-
-__device__ __forceinline__ TUnit tunit(int u, int M, float rcp) {
-  const int rest = div_small(u, M, rcp);
-  return TUnit{u - rest * M, rest & 3, (rest >> 2) & 7, rest >> 5};
-}
-
-__device__ __forceinline__ void tstage_issue(const StageArgs& a, int base, float rcp,
-                                             StageBatch& b) {
-  const int nunits = a.M * a.nbw * 32;
-  const int nthr = (int)blockDim.x;
-#pragma unroll
-  for (int i = 0; i < kStageBatch; ++i) {
-    const int u = base + i * nthr + (int)threadIdx.x;
-    const TUnit c = tunit(u < nunits ? u : 0, a.M, rcp);
-    const float* src = a.x + (size_t)x_row(a, c.m) * a.K + (size_t)(a.kb0 + c.bl) * kBlockWeights +
-                       64 * c.g + 4 * c.t;
-    b.lo[i] = *reinterpret_cast<const float4*>(src);
-    b.hi[i] = *reinterpret_cast<const float4*>(src + 32);
-  }
-}
-
-// dwords of a unit: x at block offsets 64g + {4t, 4t+2 | 4t+1, 4t+3 |
-// 32+4t, 32+4t+2 | 32+4t+1, 32+4t+3}, the order of the B operand's nibbles
-__device__ __forceinline__ void tstage_finish(const StageArgs& a, int base, const StageBatch& b) {
-  const int nunits = a.M * a.nbw * 32;
-  const int nthr = (int)blockDim.x;
-#pragma unroll
-  for (int i = 0; i < kStageBatch; ++i) {
-    const int u = base + i * nthr + (int)threadIdx.x;
-    if (u < nunits) {
-      u4_t v;
-      v.x = pack_h2((_Float16)b.lo[i].x, (_Float16)b.lo[i].z);
-      v.y = pack_h2((_Float16)b.lo[i].y, (_Float16)b.lo[i].w);
-      v.z = pack_h2((_Float16)b.hi[i].x, (_Float16)b.hi[i].z);
-      v.w = pack_h2((_Float16)b.hi[i].y, (_Float16)b.hi[i].w);
-      *reinterpret_cast<u4_t*>(a.lds_x + 16 * u) = v;
-    }
-  }
-}
-
-// Every batch but the last: issue the next batch's loads before converting
-// the current one, so that all x loads are issued before any weight load;
-// returns the base of the last batch, whose loads are in flight in cur.
-__device__ __forceinline__ int tstage_lead(const StageArgs& a, float rcp, StageBatch& cur) {
-  const int nunits = a.M * a.nbw * 32;
-  const int step = (int)blockDim.x * kStageBatch;
-  int base = 0;
-  tstage_issue(a, 0, rcp, cur);
-  for (; base + step < nunits; base += step) {
-    StageBatch next;
-    tstage_issue(a, base + step, rcp, next);
-    tstage_finish(a, base, cur);
-    cur = next;
-  }
-  return base;
-}
 
 // Sums of the rounded x over sub-blocks 2g and 2g+1 of (m, bl): entry
 // e = (bl*4 + g)*M + m, added over t = 0..7 in order. Call after a barrier.
@@ -890,17 +916,17 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
       (uint32_t)(red_base + lds_red_bytes(Mtot, waves, wsplit) + wave * 16 * kBufRowStride);
   const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s, sl0.rowreg, IDS};
   const float rcp = 1.0f / (float)M;
-  StageBatch sb;
-  const int last_base = tstage_lead(st, rcp, sb);
+  XRegs<kTiledLead> xb;
+  int xnu;
+  const int xbase = x_lead<true, kTiledLead>(st, rcp, xb, xnu);
   issue_barrier();
   int tile = (int)blockIdx.x * c.T + c.wtile;
   StageLane sl;
   StageRegs sr;
-  if (tile < ntiles && nstages > 0) {
-    stage_lane(lane, nb, min(16, N - tile * 16), wbuf, sl);
-    stage_load(slice_base + (size_t)tile * 16 * row_bytes, sl, 0, c.nbw, sr);
-  }
-  tstage_finish(st, last_base, sb);
+  first_stage(sl0.W, slice_base, tile, ntiles, nstages, nb, N, c.nbw, row_bytes, lane, wbuf, sl,
+              sr);
+  wait_vm<kStageLoads>();  // x complete; the first weight stage stays in flight
+  x_finish<true, kTiledLead>(st, xbase, xnu, xb);
   __syncthreads();
   tstage_sums(st, rcp);
   __syncthreads();
