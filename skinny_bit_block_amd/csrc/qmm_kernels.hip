@@ -179,6 +179,22 @@ __device__ __forceinline__ int div_small(int u, int d, float rcp) {
   return q;
 }
 
+// Sum over the 8 aligned lanes of a group, in every lane of it, with DPP
+// moves (VALU, no LDS traffic): quad_perm [1,0,3,2] and [2,3,0,1] leave the
+// quad's sum in each lane (fp32 addition is commutative, so all four agree),
+// row_half_mirror then adds the other quad of the eight.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  return v;
+}
+
 // Unit order of the staging loads: u = ((bl*M + m)*4 + g)*8 + t, so the 8
 // consecutive lanes t = 0..7 read one contiguous 128-byte run of a row (the
 // kernels' LDS layouts are computed from (m, bl, g, t) when storing). A probe
@@ -221,7 +237,7 @@ __device__ __forceinline__ void x_issue(const StageArgs& a, int base, int nu, fl
 //     d = 4t + c of (m, bl, g) at m*xs_m + bl*512 + g*128, dword d at position
 //     2*(d % 16) + d / 16, so lane r of a 16-lane row reads dwords r and 16 + r
 //     with one 8-byte load; sums[m][bl][j] at m*ss_m + bl*8 + j;
-//   tiled kernel (tiled_unit_store below, tstage_sums further down): unit (m, bl, g, t) at
+//   tiled kernel (tiled_unit_store below): unit (m, bl, g, t) at
 //     16*(((bl*8 + t)*4 + g)*M + m), the order the MFMA A operand reads, so
 //     the 16 lanes of a j-pair read M consecutive units (rows past M repeat
 //     real rows); sums of (m, bl, g) as a float2 at 8*((bl*4 + g)*M + m).
@@ -238,14 +254,8 @@ __device__ __forceinline__ void vector_unit_store(const StageArgs& a, int u, boo
   v.y = pack_h2(l1, l3);
   v.z = pack_h2(h0, h2);
   v.w = pack_h2(h1, h3);
-  float slo = ((float)l0 + (float)l1) + ((float)l2 + (float)l3);
-  float shi = ((float)h0 + (float)h1) + ((float)h2 + (float)h3);
-  slo += __shfl_xor(slo, 1);
-  shi += __shfl_xor(shi, 1);
-  slo += __shfl_xor(slo, 2);
-  shi += __shfl_xor(shi, 2);
-  slo += __shfl_xor(slo, 4);
-  shi += __shfl_xor(shi, 4);
+  const float slo = sum8(((float)l0 + (float)l1) + ((float)l2 + (float)l3));
+  const float shi = sum8(((float)h0 + (float)h1) + ((float)h2 + (float)h3));
   if (ok) {
     uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
     const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
@@ -261,17 +271,28 @@ __device__ __forceinline__ void vector_unit_store(const StageArgs& a, int u, boo
 }
 
 // dwords of a unit: x at block offsets 64g + {4t, 4t+2 | 4t+1, 4t+3 |
-// 32+4t, 32+4t+2 | 32+4t+1, 32+4t+3}, the order of the B operand's nibbles
+// 32+4t, 32+4t+2 | 32+4t+1, 32+4t+3}, the order of the B operand's nibbles.
+// The sub-block sums come from the same rounded values: a unit's four, then a
+// DPP sum over the eight lanes t = 0..7 of its (m, bl, g) group, which are
+// adjacent in the load order (every lane takes part; only valid units store).
 __device__ __forceinline__ void tiled_unit_store(const StageArgs& a, int u, bool ok, float rcp,
                                                  const float4& lo, const float4& hi) {
+  const XUnit c = xunit(ok ? u : 0, a.M, rcp);
+  const _Float16 l0 = (_Float16)lo.x, l1 = (_Float16)lo.y, l2 = (_Float16)lo.z,
+                 l3 = (_Float16)lo.w;
+  const _Float16 h0 = (_Float16)hi.x, h1 = (_Float16)hi.y, h2 = (_Float16)hi.z,
+                 h3 = (_Float16)hi.w;
+  const float slo = sum8(((float)l0 + (float)l1) + ((float)l2 + (float)l3));
+  const float shi = sum8(((float)h0 + (float)h1) + ((float)h2 + (float)h3));
   if (ok) {
-    const XUnit c = xunit(u, a.M, rcp);
     u4_t v;
-    v.x = pack_h2((_Float16)lo.x, (_Float16)lo.z);
-    v.y = pack_h2((_Float16)lo.y, (_Float16)lo.w);
-    v.z = pack_h2((_Float16)hi.x, (_Float16)hi.z);
-    v.w = pack_h2((_Float16)hi.y, (_Float16)hi.w);
+    v.x = pack_h2(l0, l2);
+    v.y = pack_h2(l1, l3);
+    v.z = pack_h2(h0, h2);
+    v.w = pack_h2(h1, h3);
     *reinterpret_cast<u4_t*>(a.lds_x + 16 * (((c.bl * 8 + c.t) * 4 + c.g) * a.M + c.m)) = v;
+    if (c.t == 0)
+      *reinterpret_cast<float2*>(a.lds_s + 2 * ((c.bl * 4 + c.g) * a.M + c.m)) = float2{slo, shi};
   }
 }
 
@@ -756,29 +777,8 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
 }
 
 // --------------------------------------------------------------------- tiled
-// Staging of the tiled kernel's activations: unit u = ((bl*8 + t)*4 + g)*M + m
-// goes to LDS byte 16u, so consecutive threads write consecutive units. The
-// sub-block sums are a second pass over the staged binary16 values.
-
-// Sums of the rounded x over sub-blocks 2g and 2g+1 of (m, bl): entry
-// e = (bl*4 + g)*M + m, added over t = 0..7 in order. Call after a barrier.
-__device__ __forceinline__ void tstage_sums(const StageArgs& a, float rcp) {
-  const int nent = a.M * a.nbw * 4;
-  for (int e = (int)threadIdx.x; e < nent; e += (int)blockDim.x) {
-    const int rest = div_small(e, a.M, rcp);
-    const int m = e - rest * a.M, g = rest & 3, bl = rest >> 2;
-    float slo = 0.f, shi = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u4_t v =
-          *reinterpret_cast<const u4_t*>(a.lds_x + 16 * (((bl * 8 + t) * 4 + g) * a.M + m));
-      slo += (f16_lo(v.x) + f16_hi(v.x)) + (f16_lo(v.y) + f16_hi(v.y));
-      shi += (f16_lo(v.z) + f16_hi(v.z)) + (f16_lo(v.w) + f16_hi(v.w));
-    }
-    a.lds_s[2 * e] = slo;
-    a.lds_s[2 * e + 1] = shi;
-  }
-}
+// The tiled kernel's activations are staged by x_lead / tiled_unit_store
+// above: unit (m, bl, g, t) at LDS byte 16*(((bl*8 + t)*4 + g)*M + m).
 
 template <int MT>
 __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLane& hl, const char* const (&xa)[MT],
@@ -919,8 +919,6 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
               sr);
   wait_vm<kStageLoads>();  // x complete; the first weight stage stays in flight
   x_finish<true, kTiledLead>(st, xbase, xnu, rcp, xb);
-  __syncthreads();
-  tstage_sums(st, rcp);
   __syncthreads();
 
   const HeaderLane hl = header_lane(g);
