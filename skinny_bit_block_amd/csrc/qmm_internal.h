@@ -51,17 +51,27 @@ inline int lds_ss_m(int nbw, int kernel) { return kernel == 1 ? nbw * 8 + 2 : nb
 // Per-wavefront transpose buffer of the weight stream: 16 rows x (4 blocks =
 // 36 chunks of 16 B + one chunk of padding).
 constexpr int kWaveBufBytes = 16 * 16 * 37;
-// LDS of a workgroup: staged x, sub-block sums, then (16-byte aligned) the
-// buffer of the in-workgroup reduction when wsplit > 1 (two iterations' worth,
-// 16 floats per row m, tile group and slice), then the per-wave weight buffers.
-__host__ __device__ inline int lds_red_base(int M, int xs_m, int ss_m) {
-  return (M * xs_m + M * ss_m * 4 + 15) & ~15;
+// Row slots of the tiled kernel's staged x: M rounded up to a power of two
+// (16 or 32 above 8 rows), so that its XOR swizzle of the row slot stays
+// inside the slots; the row-vector kernel stores exactly M rows.
+__host__ __device__ inline int tiled_x_rows(int M) {
+  return M > 16 ? 32 : (M > 8 ? 16 : (M > 4 ? 8 : (M > 2 ? 4 : M)));
+}
+__host__ __device__ inline int x_rows(int M, int kernel) {
+  return kernel == 1 ? M : tiled_x_rows(M);
+}
+// LDS of a workgroup: staged x (Mx row slots), sub-block sums (M rows), then
+// (16-byte aligned) the buffer of the in-workgroup reduction when wsplit > 1
+// (two iterations' worth, 16 floats per row m, tile group and slice), then the
+// per-wave weight buffers.
+__host__ __device__ inline int lds_red_base(int Mx, int M, int xs_m, int ss_m) {
+  return (Mx * xs_m + M * ss_m * 4 + 15) & ~15;
 }
 __host__ __device__ inline int lds_red_bytes(int M, int waves, int wsplit) {
   return wsplit > 1 ? 2 * waves * M * 16 * 4 : 0;
 }
 inline int lds_bytes(int M, int nbw, int waves, int wsplit, int kernel) {
-  return lds_red_base(M, lds_xs_m(nbw, kernel), lds_ss_m(nbw, kernel)) +
+  return lds_red_base(x_rows(M, kernel), M, lds_xs_m(nbw, kernel), lds_ss_m(nbw, kernel)) +
          lds_red_bytes(M, waves, wsplit) + waves * kWaveBufBytes;
 }
 

@@ -153,12 +153,13 @@ constexpr int kTiledLead = 16;
 
 template <int U>
 struct XRegs {
-  float4 lo[U], hi[U];
+  f4_t lo[U], hi[U];  // native vectors (HIP's float4 wrapper kept them out of registers)
 };
 
 struct StageArgs {
   const float* x;
   int M, K, kb0, nbw, xs_m, ss_m;
+  int Mx;  // tiled kernel: row slots of the staged x (tiled_x_rows)
   char* lds_x;
   float* lds_s;
   int rowreg;  // with an expert map: lane k holds the x row of local row k
@@ -180,19 +181,32 @@ __device__ __forceinline__ int div_small(int u, int d, float rcp) {
 }
 
 // Sum over the 8 aligned lanes of a group, in every lane of it, with DPP
-// moves (VALU, no LDS traffic): quad_perm [1,0,3,2] and [2,3,0,1] leave the
-// quad's sum in each lane (fp32 addition is commutative, so all four agree),
-// row_half_mirror then adds the other quad of the eight.
+// (VALU, no LDS traffic; the compiler folds each move into a v_add_f32_dpp):
+// quad_perm [1,0,3,2] and [2,3,0,1] leave the quad's sum in each lane (fp32
+// addition is commutative, so all four agree), row_half_mirror then adds the
+// other quad of the eight.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float sum8(float v) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_mov<0x141>(v);  // row_half_mirror
   return v;
+}
+
+// Two fp32 values rounded to binary16 (nearest-even) and packed, a in the
+// low half: one v_cvt_pk_f16_f32.
+typedef float f2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+}
+// c + the two binary16 values of p, in fp32 (one v_dot2 with ones).
+__device__ __forceinline__ float hsum2(uint32_t p, float c) {
+  const h2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, p), ones, c, false);
 }
 
 // Unit order of the staging loads: u = ((bl*M + m)*4 + g)*8 + t, so the 8
@@ -210,105 +224,122 @@ __device__ __forceinline__ XUnit xunit(int u, int M, float rcp) {
   return XUnit{rest - bl * M, (u >> 3) & 3, u & 7, bl};
 }
 
-// First of the 8 fp32 values of unit u (the other four are 32 further on).
-__device__ __forceinline__ const float* unit_src(const StageArgs& a, int u, float rcp) {
-  const XUnit c = xunit(u, a.M, rcp);
-  return a.x + (size_t)x_row(a, c.m) * a.K + (size_t)(a.kb0 + c.bl) * kBlockWeights + 64 * c.g +
-         4 * c.t;
+// A thread's units of one chunk are base + j*nthr + threadIdx.x, j = 0, 1, ...
+// Their t and g are the thread's own (nthr is a multiple of 32); (m, bl)
+// advance by the quotient and remainder of nthr/32 by M at each step.
+struct XWalk {
+  int m, bl;
+  int dq, dr;
+};
+__device__ __forceinline__ XWalk xwalk(int base, int M, float rcp) {
+  const int rest = (base + (int)threadIdx.x) >> 5;
+  const int bl = div_small(rest, M, rcp);
+  const int s = (int)blockDim.x >> 5;
+  const int dq = div_small(s, M, rcp);
+  return XWalk{rest - bl * M, bl, dq, s - dq * M};
+}
+__device__ __forceinline__ void xstep(XWalk& w, int M) {
+  w.m += w.dr;
+  w.bl += w.dq;
+  if (w.m >= M) {
+    w.m -= M;
+    ++w.bl;
+  }
 }
 
-template <bool TILED, int U>
+// Tiled x layout: unit (m, bl, g, t) of c-row c = (bl*8 + t)*4 + g sits in
+// row slot m ^ xswz(t, g, Mx) of that c-row (Mx slots of 16 B). Without the
+// swizzle the staging stores, whose 16-lane groups take t = 0..7 and two g of
+// one row, all fall into the same LDS banks for Mx >= 16 (a probe: 64 cycles
+// per store instead of 4.6); with it they cover 16 distinct 16-byte slots
+// (Mx >= 8; 2-way at most below), while the MFMA reads of a c-row (16 rows at
+// fixed t, g) remain a permutation of 16 slots (measured at the same cost).
+__device__ __forceinline__ int xswz(int t, int g, int Mx) {
+  return Mx >= 16 ? ((2 * t + (g & 1)) & 15) : (t & (Mx - 1));
+}
+
+// Loads of a chunk: nu units per thread. Lanes past the last unit re-read a
+// unit of the slice (row M-1, last block) and store nothing.
+template <int U>
 __device__ __forceinline__ void x_issue(const StageArgs& a, int base, int nu, float rcp,
                                         XRegs<U>& b) {
   const int last = a.M * a.nbw * 32 - 1;
   const int nthr = (int)blockDim.x;
+  const int t = (int)threadIdx.x & 7, g = ((int)threadIdx.x >> 3) & 3;
+  const uint32_t c0 = (uint32_t)(a.kb0 * kBlockWeights + 64 * g + 4 * t);
+  const uint32_t clamp = (uint32_t)x_row(a, a.M - 1) * (uint32_t)a.K +
+                         (uint32_t)(a.nbw - 1) * kBlockWeights + c0;
+  XWalk w = xwalk(base, a.M, rcp);
 #pragma unroll
   for (int j = 0; j < U; ++j) {
     if (j < nu) {  // uniform across the workgroup
-      const float* src = unit_src(a, min(base + j * nthr + (int)threadIdx.x, last), rcp);
-      b.lo[j] = *reinterpret_cast<const float4*>(src);
-      b.hi[j] = *reinterpret_cast<const float4*>(src + 32);
+      const int u = base + j * nthr + (int)threadIdx.x;
+      const uint32_t off =
+          u <= last ? (uint32_t)x_row(a, w.m) * (uint32_t)a.K + (uint32_t)(w.bl << 8) + c0 : clamp;
+      const float* src = a.x + off;
+      b.lo[j] = *reinterpret_cast<const f4_t*>(src);
+      b.hi[j] = *reinterpret_cast<const f4_t*>(src + 32);
+      xstep(w, a.M);
     }
   }
 }
 
 // Layouts of the staged activations (units of 16 B = 8 binary16 values):
-//   row-vector kernel (vector_unit_store below): the 32 dwords
-//     d = 4t + c of (m, bl, g) at m*xs_m + bl*512 + g*128, dword d at position
-//     2*(d % 16) + d / 16, so lane r of a 16-lane row reads dwords r and 16 + r
-//     with one 8-byte load; sums[m][bl][j] at m*ss_m + bl*8 + j;
-//   tiled kernel (tiled_unit_store below): unit (m, bl, g, t) at
-//     16*(((bl*8 + t)*4 + g)*M + m), the order the MFMA A operand reads, so
-//     the 16 lanes of a j-pair read M consecutive units (rows past M repeat
-//     real rows); sums of (m, bl, g) as a float2 at 8*((bl*4 + g)*M + m).
-__device__ __forceinline__ void vector_unit_store(const StageArgs& a, int u, bool ok, float rcp,
-                                                  const float4& lo, const float4& hi) {
-  const XUnit c = xunit(ok ? u : 0, a.M, rcp);
-  const int t = c.t, g = c.g, bl = c.bl, m = c.m;
-  const _Float16 l0 = (_Float16)lo.x, l1 = (_Float16)lo.y, l2 = (_Float16)lo.z,
-                 l3 = (_Float16)lo.w;
-  const _Float16 h0 = (_Float16)hi.x, h1 = (_Float16)hi.y, h2 = (_Float16)hi.z,
-                 h3 = (_Float16)hi.w;
-  u4_t v;
-  v.x = pack_h2(l0, l2);
-  v.y = pack_h2(l1, l3);
-  v.z = pack_h2(h0, h2);
-  v.w = pack_h2(h1, h3);
-  const float slo = sum8(((float)l0 + (float)l1) + ((float)l2 + (float)l3));
-  const float shi = sum8(((float)h0 + (float)h1) + ((float)h2 + (float)h3));
-  if (ok) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + m * a.xs_m + bl * 512 + g * 128);
-    const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // position of dword 4t
-    dst[p0] = v.x;
-    dst[p0 + 2] = v.y;
-    dst[p0 + 4] = v.z;
-    dst[p0 + 6] = v.w;
-    if (t == 0) {
-      a.lds_s[m * a.ss_m + bl * 8 + 2 * g] = slo;
-      a.lds_s[m * a.ss_m + bl * 8 + 2 * g + 1] = shi;
-    }
-  }
-}
-
+//   row-vector kernel: the 32 dwords d = 4t + c of (m, bl, g) at
+//     m*xs_m + bl*512 + g*128, dword d at position 2*(d % 16) + d / 16, so
+//     lane r of a 16-lane row reads dwords r and 16 + r with one 8-byte load;
+//     sums[m][bl][j] at m*ss_m + bl*8 + j;
+//   tiled kernel: unit (m, bl, g, t) at
+//     16*(((bl*8 + t)*4 + g)*Mx + (m ^ xswz(t, g, Mx))), so the 16 lanes of a
+//     j-pair read the units of one c-row (rows past M repeat real rows);
+//     sums of (m, bl, g) as a float2 at 8*((bl*4 + g)*M + m).
 // dwords of a unit: x at block offsets 64g + {4t, 4t+2 | 4t+1, 4t+3 |
 // 32+4t, 32+4t+2 | 32+4t+1, 32+4t+3}, the order of the B operand's nibbles.
 // The sub-block sums come from the same rounded values: a unit's four, then a
 // DPP sum over the eight lanes t = 0..7 of its (m, bl, g) group, which are
 // adjacent in the load order (every lane takes part; only valid units store).
-__device__ __forceinline__ void tiled_unit_store(const StageArgs& a, int u, bool ok, float rcp,
-                                                 const float4& lo, const float4& hi) {
-  const XUnit c = xunit(ok ? u : 0, a.M, rcp);
-  const _Float16 l0 = (_Float16)lo.x, l1 = (_Float16)lo.y, l2 = (_Float16)lo.z,
-                 l3 = (_Float16)lo.w;
-  const _Float16 h0 = (_Float16)hi.x, h1 = (_Float16)hi.y, h2 = (_Float16)hi.z,
-                 h3 = (_Float16)hi.w;
-  const float slo = sum8(((float)l0 + (float)l1) + ((float)l2 + (float)l3));
-  const float shi = sum8(((float)h0 + (float)h1) + ((float)h2 + (float)h3));
-  if (ok) {
-    u4_t v;
-    v.x = pack_h2(l0, l2);
-    v.y = pack_h2(l1, l3);
-    v.z = pack_h2(h0, h2);
-    v.w = pack_h2(h1, h3);
-    *reinterpret_cast<u4_t*>(a.lds_x + 16 * (((c.bl * 8 + c.t) * 4 + c.g) * a.M + c.m)) = v;
-    if (c.t == 0)
-      *reinterpret_cast<float2*>(a.lds_s + 2 * ((c.bl * 4 + c.g) * a.M + c.m)) = float2{slo, shi};
-  }
-}
-
 template <bool TILED, int U>
 __device__ __forceinline__ void x_finish(const StageArgs& a, int base, int nu, float rcp,
                                          const XRegs<U>& b) {
   const int nunits = a.M * a.nbw * 32;
   const int nthr = (int)blockDim.x;
+  const int t = (int)threadIdx.x & 7, g = ((int)threadIdx.x >> 3) & 3;
+  const int sw = xswz(t, g, a.Mx);
+  const int cslot = (4 * t + g) * a.Mx;
+  const int lgblk = 5 + (31 - __builtin_clz(a.Mx));  // slots per super-block: 32 * Mx
+  const int p0 = t < 4 ? 8 * t : 8 * (t - 4) + 1;  // row-vector: position of dword 4t
+  XWalk w = xwalk(base, a.M, rcp);
 #pragma unroll
   for (int j = 0; j < U; ++j) {
     if (j < nu) {  // uniform
       const int u = base + j * nthr + (int)threadIdx.x;
-      if (TILED)
-        tiled_unit_store(a, u, u < nunits, rcp, b.lo[j], b.hi[j]);
-      else
-        vector_unit_store(a, u, u < nunits, rcp, b.lo[j], b.hi[j]);
+      u4_t v;
+      v.x = cvt_pk(b.lo[j][0], b.lo[j][2]);
+      v.y = cvt_pk(b.lo[j][1], b.lo[j][3]);
+      v.z = cvt_pk(b.hi[j][0], b.hi[j][2]);
+      v.w = cvt_pk(b.hi[j][1], b.hi[j][3]);
+      const float slo = sum8(hsum2(v.x, hsum2(v.y, 0.f)));
+      const float shi = sum8(hsum2(v.z, hsum2(v.w, 0.f)));
+      if (u < nunits) {
+        if (TILED) {
+          const int slot = (w.bl << lgblk) + cslot + (w.m ^ sw);
+          *reinterpret_cast<u4_t*>(a.lds_x + 16 * slot) = v;
+          if (t == 0)
+            *reinterpret_cast<float2*>(a.lds_s + 2 * ((w.bl * 4 + g) * a.M + w.m)) =
+                float2{slo, shi};
+        } else {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(a.lds_x + w.m * a.xs_m + w.bl * 512 + g * 128);
+          dst[p0] = v.x;
+          dst[p0 + 2] = v.y;
+          dst[p0 + 4] = v.z;
+          dst[p0 + 6] = v.w;
+          if (t == 0) {
+            a.lds_s[w.m * a.ss_m + w.bl * 8 + 2 * g] = slo;
+            a.lds_s[w.m * a.ss_m + w.bl * 8 + 2 * g + 1] = shi;
+          }
+        }
+      }
+      xstep(w, a.M);
     }
   }
 }
@@ -321,10 +352,10 @@ __device__ __forceinline__ int x_lead(const StageArgs& a, float rcp, XRegs<U>& b
   int left = (a.M * a.nbw * 32 + nthr - 1) / nthr;
   int base = 0;
   for (; left > U; left -= U, base += U * nthr) {
-    x_issue<TILED, U>(a, base, U, rcp, b);
+    x_issue<U>(a, base, U, rcp, b);
     x_finish<TILED, U>(a, base, U, rcp, b);
   }
-  x_issue<TILED, U>(a, base, left, rcp, b);
+  x_issue<U>(a, base, left, rcp, b);
   nu = left;
   return base;
 }
@@ -692,11 +723,11 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
 
   char* lds_x = lds;
   float* lds_s = reinterpret_cast<float*>(lds + M * xs_m);
-  const int red_base = lds_red_base(M, xs_m, ss_m);
+  const int red_base = lds_red_base(M, M, xs_m, ss_m);
   float* red = reinterpret_cast<float*>(lds + red_base);
   const uint32_t wbuf =
       (uint32_t)(red_base + lds_red_bytes(M, waves, wsplit) + wave * 16 * kBufRowStride);
-  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s, 0, false};
+  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, M, lds_x, lds_s, 0, false};
   XRegs<kVectorLead> xb;
   int xnu;
   const float rcp = 1.0f / (float)M;
@@ -777,12 +808,13 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
 }
 
 // --------------------------------------------------------------------- tiled
-// The tiled kernel's activations are staged by x_lead / tiled_unit_store
+// The tiled kernel's activations are staged by x_lead / x_finish
 // above: unit (m, bl, g, t) at LDS byte 16*(((bl*8 + t)*4 + g)*M + m).
 
 template <int MT>
-__device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLane& hl, const char* const (&xa)[MT],
-                                            const float* const (&sa)[MT], int bl, int M,
+__device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLane& hl,
+                                            const char* lds_x, const int (&xo)[MT][8],
+                                            const float* const (&sa)[MT], int bl, int M, int Mx,
                                             f4_t (&acc)[MT]) {
   const Header h = decode_header(br.hd, hl);
   const _Float16 sa16 = (_Float16)(float)(h.sc_a * 1024u);  // q*2^-24 -> q*sc*2^-14
@@ -805,12 +837,12 @@ __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLan
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const char* xp = xa[mt] + bl * 512 * M;
+    const char* xp = lds_x + bl * 512 * Mx;
     f4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(xp + t * 64 * M)), bw[t], c, 0,
+          __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(xp + xo[mt][t])), bw[t], c, 0,
           0, 0);
     f4_t a = acc[mt];
     a[0] = fmaf(dd, c[0], a[0]);
@@ -900,13 +932,14 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   const uint8_t* slice_base = sl0.W + (size_t)c.kb0 * kBlockBytes;
 
   // LDS regions are laid out for Mtot rows; this slot uses the first M
+  const int Mx = tiled_x_rows(Mtot);
   char* lds_x = lds;
-  float* lds_s = reinterpret_cast<float*>(lds + Mtot * xs_m);
-  const int red_base = lds_red_base(Mtot, xs_m, ss_m);
+  float* lds_s = reinterpret_cast<float*>(lds + Mx * xs_m);
+  const int red_base = lds_red_base(Mx, Mtot, xs_m, ss_m);
   float* red = reinterpret_cast<float*>(lds + red_base);
   const uint32_t wbuf =
       (uint32_t)(red_base + lds_red_bytes(Mtot, waves, wsplit) + wave * 16 * kBufRowStride);
-  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, lds_x, lds_s, sl0.rowreg, IDS};
+  const StageArgs st{x, M, K, c.kb0_wg, c.nbw_wg, xs_m, ss_m, Mx, lds_x, lds_s, sl0.rowreg, IDS};
   const float rcp = 1.0f / (float)M;
   XRegs<kTiledLead> xb;
   int xnu;
@@ -924,14 +957,16 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   const HeaderLane hl = header_lane(g);
   // A-operand row this lane reads in each 16-row MFMA tile. An MFMA output row
   // depends only on its A row and rows past M are never stored, so padded
-  // rows re-read a real row of the same tile.
-  const char* xa[MT];
+  // rows re-read a real row of the same tile. xo: the row's unit of c-row
+  // 4t + g within a super-block (swizzled slot), per tile and t.
+  int xo[MT][8];
   const float* sa[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int rows = min(M - 16 * mt, 16);
     const int m = 16 * mt + r % rows;
-    xa[mt] = lds_x + 16 * (g * M + m);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xo[mt][t] = 16 * ((4 * t + g) * Mx + (m ^ xswz(t, g, Mx)));
     sa[mt] = lds_s + 2 * (g * M + m);
   }
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
@@ -970,7 +1005,7 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
         if (bl < c.nbw) {
           BlockRegs br;
           read_block(rowbuf, g, j, br);
-          tiled_block<MT>(br, hl, xa, sa, c.bl_off + bl, M, acc);
+          tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl, M, Mx, acc);
         }
       }
     }

@@ -125,7 +125,8 @@ def test_launch_shapes(h, M, kernel, shape):
 @pytest.mark.parametrize("shape,wsplit", [((2, 2, 0), 2), ((4, 4, 0), 4), ((5, 5, 0), 5),
                                           ((4, 8, 0), 4), ((8, 4, 0), 4), ((6, 3, 0), 3),
                                           ((8, 8, 3), 2), ((4, 10, 1), 2), ((3, 3, 2), 3),
-                                          ((8, 10, 0), 8), ((7, 7, 0), 7)])
+                                          ((8, 10, 0), 8), ((7, 7, 0), 7),
+                                          ((2, 10, 0), 2), ((4, 10, 0), 4)])
 @pytest.mark.parametrize("M,kernel", [(1, sbb.KERNEL_VECTOR), (5, sbb.KERNEL_VECTOR),
                                       (3, sbb.KERNEL_TILED), (12, sbb.KERNEL_TILED),
                                       (20, sbb.KERNEL_TILED)])
