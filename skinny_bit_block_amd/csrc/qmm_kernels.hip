@@ -775,13 +775,23 @@ __global__ void __launch_bounds__(512) qmm_vector_kernel(const float* __restrict
         if (nsn == 0 && N - nt * 16 < 16) stage_lane(lane, nb, N - nt * 16, wbuf, sl);
         stage_load(slice_base + (size_t)nt * 16 * row_bytes, sl, nsn, c.nbw, sr);
       }
+      const int bl0 = cs * kStageBlocks;
+      if (bl0 + kStageBlocks <= c.nbw) {
+        // full stage: one basic block, so the scheduler can overlap blocks
 #pragma unroll
-      for (int j = 0; j < kStageBlocks; ++j) {
-        const int bl = cs * kStageBlocks + j;
-        if (bl < c.nbw) {
+        for (int j = 0; j < kStageBlocks; ++j) {
           BlockRegs br;
           read_block(rowbuf, g, j, br);
-          vector_block<M>(br, hl, xl, sg, c.bl_off + bl, xs_m, ss_m, acc);
+          vector_block<M>(br, hl, xl, sg, c.bl_off + bl0 + j, xs_m, ss_m, acc);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kStageBlocks; ++j) {
+          if (bl0 + j < c.nbw) {
+            BlockRegs br;
+            read_block(rowbuf, g, j, br);
+            vector_block<M>(br, hl, xl, sg, c.bl_off + bl0 + j, xs_m, ss_m, acc);
+          }
         }
       }
     }
@@ -999,13 +1009,23 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
         if (nsn == 0 && N - nt * 16 < 16) stage_lane(lane, nb, N - nt * 16, wbuf, sl);
         stage_load(slice_base + (size_t)nt * 16 * row_bytes, sl, nsn, c.nbw, sr);
       }
+      const int bl0 = cs * kStageBlocks;
+      if (bl0 + kStageBlocks <= c.nbw) {
+        // full stage: one basic block, so the scheduler can overlap blocks
 #pragma unroll
-      for (int j = 0; j < kStageBlocks; ++j) {
-        const int bl = cs * kStageBlocks + j;
-        if (bl < c.nbw) {
+        for (int j = 0; j < kStageBlocks; ++j) {
           BlockRegs br;
           read_block(rowbuf, g, j, br);
-          tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl, M, Mx, acc);
+          tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kStageBlocks; ++j) {
+          if (bl0 + j < c.nbw) {
+            BlockRegs br;
+            read_block(rowbuf, g, j, br);
+            tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
+          }
         }
       }
     }
