@@ -7,6 +7,9 @@ no code with the HIP library and imports nothing from it.
 
 Pins: see qk_oracle.c. GGUF file compatibility of the byte layout is parity
 unpinned (no GGUF file is available to compare against).
+
+oracle.nvfp4 is the oracle of the block-scaled FP4 product (numpy, binary64;
+its header gives the format's sources and pins).
 """
 import ctypes
 import os

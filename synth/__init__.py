@@ -26,7 +26,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 DEFAULT_SEED = 20261202
 BLOCK_BYTES = 144
 BLOCK_WEIGHTS = 256
-FIELD_BYTES, FIELD_D, FIELD_DMIN, FIELD_X = 1, 2, 3, 4
+FIELD_BYTES, FIELD_D, FIELD_DMIN, FIELD_X, FIELD_FP4_ELEMS, FIELD_FP4_SCALES = 1, 2, 3, 4, 5, 6
 
 
 def build():
@@ -52,6 +52,9 @@ def _load():
         lib.synth_acts.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_double, ctypes.c_void_p]
         lib.synth_acts.restype = ctypes.c_int
+        lib.synth_nvfp4.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_nvfp4.restype = ctypes.c_int
         lib.synth_f64_to_f16.argtypes = [ctypes.c_double]
         lib.synth_f64_to_f16.restype = ctypes.c_uint16
         lib.synth_word.argtypes = [ctypes.c_uint64] * 4
@@ -91,6 +94,22 @@ def acts(M, K, tensor, seed=DEFAULT_SEED, scale=1.0, out=None):
     if rc:
         raise RuntimeError("synth_acts failed")
     return out
+
+
+def nvfp4(n_rows, K, tensor, seed=DEFAULT_SEED):
+    """Block-scaled FP4 weights in the usual two-array layout: (elems uint8
+    [n_rows, K/2], two 4-bit codes per byte, element 2i in the low nibble;
+    scales uint8 [n_rows, K/16], one 8-bit scale code per 16 elements).
+    Random bit fields only; see synth_nvfp4 in synth.c."""
+    if K <= 0 or K % 16:
+        raise ValueError("K must be a positive multiple of 16")
+    elems = np.empty((int(n_rows), int(K) // 2), dtype=np.uint8)
+    scales = np.empty((int(n_rows), int(K) // 16), dtype=np.uint8)
+    rc = _load().synth_nvfp4(seed, tensor, int(n_rows), int(K), elems.ctypes.data,
+                             scales.ctypes.data)
+    if rc:
+        raise RuntimeError("synth_nvfp4 failed")
+    return elems, scales
 
 
 def f64_to_f16_bits(v):

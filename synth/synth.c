@@ -33,7 +33,7 @@
 
 #define SM_GAMMA 0x9E3779B97F4A7C15ULL
 
-enum { FIELD_BYTES = 1, FIELD_D = 2, FIELD_DMIN = 3, FIELD_X = 4 };
+enum { FIELD_BYTES = 1, FIELD_D = 2, FIELD_DMIN = 3, FIELD_X = 4, FIELD_FP4_ELEMS = 5, FIELD_FP4_SCALES = 6 };
 
 static inline uint64_t sm_mix(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
@@ -105,6 +105,31 @@ int synth_weights(uint64_t seed, uint64_t tensor, int64_t n_rows, int64_t K,
     p[1] = (uint8_t)(d >> 8);
     p[2] = (uint8_t)(dm & 0xFF);
     p[3] = (uint8_t)(dm >> 8);
+  }
+  return 0;
+}
+
+/* Block-scaled FP4 weights in the usual two-array layout: elems n_rows x K/2
+   bytes of 4-bit codes (uniform random bytes, two codes per byte), scales
+   n_rows x K/16 bytes, one 8-bit scale code per 16 elements with a uniform
+   exponent field 0..14 and mantissa field 0..7 and the sign bit clear (so no
+   code is NaN; zero and subnormal scales occur). Only random bit fields: the
+   values these codes stand for are not computed here. */
+int synth_nvfp4(uint64_t seed, uint64_t tensor, int64_t n_rows, int64_t K, uint8_t* elems,
+                uint8_t* scales) {
+  if (K <= 0 || K % 16 != 0 || n_rows < 0 || !elems || !scales) return -1;
+  const int64_t ne = n_rows * (K / 2), ns = n_rows * (K / 16);
+  const uint64_t ke = sm_key(seed, tensor, FIELD_FP4_ELEMS);
+  const uint64_t ks = sm_key(seed, tensor, FIELD_FP4_SCALES);
+#pragma omp parallel for schedule(static)
+  for (int64_t w = 0; w < (ne + 7) / 8; ++w) {
+    const uint64_t r = sm_word(ke, (uint64_t)w);
+    for (int t = 0; t < 8 && 8 * w + t < ne; ++t) elems[8 * w + t] = (uint8_t)(r >> (8 * t));
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < ns; ++i) {
+    const uint64_t r = sm_word(ks, (uint64_t)i);
+    scales[i] = (uint8_t)(((r % 15u) << 3) | ((r >> 8) & 7u));
   }
   return 0;
 }
