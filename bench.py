@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ids", action="store_true", help="skip the expert-indexed record")
+    ap.add_argument("--no-fp4", action="store_true", help="skip the block-scaled FP4 record")
     ap.add_argument("--no-eager", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="one allocation per matrix instead of one weight arena")
@@ -146,7 +147,7 @@ class Pass:
     def kernel_symbol(self, M, N, K):
         p = self.plan(M, N, K)
         if p["kernel"] == self.sbb.KERNEL_TILED:
-            return "qmm_tiled_kernel<%d, false>" % (1 if M <= 16 else 2)
+            return "qmm_tiled_kernel<%d, false, 0>" % (1 if M <= 16 else 2)
         return "qmm_vector_kernel<%d>" % M
 
 
@@ -332,6 +333,59 @@ def ids_measure(torch, sbb, synth, acc, h, reps=5):
                         "rows over distinct experts", "per_m": out}
 
 
+def nvfp4_measure(torch, sbb, synth, acc, h, reps=5):
+    """Block-scaled FP4 product on the shapes the pages bench it on (gate+up
+    34816x5120 and a 248320-row lm_head, K=5120, at 1 and 7 rows). Weight bytes
+    are counted per call (144 per 256 weights); each timed sequence walks
+    distinct device copies of the matrix (8 of gate+up, 2 of lm_head) so the
+    weights stream from HBM, replayed as a graph."""
+    import numpy as np
+    out = {}
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda:0")
+    for name, N, K, copies in (("gate_up", 34816, 5120, 8), ("lm_head_248320", 248320, 5120, 2)):
+        elems, scales = synth.nvfp4(N, K, tensor=92000 + N % 1000, seed=SEED)
+        groups = torch.from_numpy(sbb.qmm_nvfp4_repack(elems, scales, N, K).reshape(-1))
+        del elems, scales
+        Ws = [groups.to(dev) for _ in range(copies)]
+        del groups
+        wb = acc.weight_bytes(N, K)
+        res = {}
+        for M in (1, 7):
+            x = torch.from_numpy(synth.acts(M, K, tensor=93000 + M, seed=SEED)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+            def go(sp):
+                for W in Ws:
+                    rc = sbb.qmm_run_nvfp4_raw(h, x.data_ptr(), W.data_ptr(), 0.5, y.data_ptr(),
+                                               M, N, K, sp)
+                    if rc:
+                        raise RuntimeError(sbb.qmm_status_string(rc))
+
+            go(stream.cuda_stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                go(torch.cuda.current_stream().cuda_stream)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / reps / len(Ws) * 1e-3
+            acc.check_roofline(wb, t, what="nvfp4 %s M=%d" % (name, M))
+            res[str(M)] = {"us_per_call": round(t * 1e6, 2), "weight_gbs": round(acc.gbs(wb, t), 1),
+                           "pct_hbm_peak": round(acc.pct_of(wb, t, 8e12), 2)}
+        out[name] = {"N": N, "K": K, "weight_bytes": wb, "per_m": res}
+        del Ws
+        torch.cuda.empty_cache()
+    return {"workload": "block-scaled FP4 (E2M1 elements, E4M3 scale per 16, fp32 tensor scale), "
+                        "seeded random codes, 144-byte groups", "shapes": out}
+
+
 def mode_pass(args, torch, sbb, synth, acc):
     ms = [int(v) for v in args.ms.split(",")]
     P = Pass(torch, sbb, synth, acc, ms, args.layers, arena=not args.separate)
@@ -371,6 +425,9 @@ def mode_pass(args, torch, sbb, synth, acc):
     if not args.no_ids:
         log("expert-indexed product...")
         out["ids"] = ids_measure(torch, sbb, synth, acc, P.h)
+    if not args.no_fp4:
+        log("block-scaled FP4 product...")
+        out["nvfp4"] = nvfp4_measure(torch, sbb, synth, acc, P.h)
     value = acc.gbs(P.weight_bytes * len(ms), ms_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

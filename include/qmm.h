@@ -114,6 +114,40 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y,
 int qmm_run_ids(qmm_handle h, const float* x, const void* W_experts, const int32_t* ids,
                 int64_t E, float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* Block-scaled FP4 weights ("NVFP4"), the second weight format. The pages
+ * measure a W4A16 product over it (FlashRT issue #153: the NVFP4 W4A16 GEMM
+ * and its per-shape bench of lm_head and gate+up at 1 and 7 rows) without
+ * defining its bits; those are public: elements FP4 E2M1 (OCP Microscaling
+ * Formats v1.0: sign, 2 exponent bits with bias 1, 1 mantissa bit), one FP8
+ * E4M3 scale (OCP OFP8: bias 7, S.1111.111 = NaN) per 16 consecutive elements
+ * of a row, one fp32 tensor scale; w = tensor_scale * scale * element.
+ *
+ * The library streams them in groups of 256 weights in 144 bytes, the
+ * geometry of the 4.5-bit super-blocks: per row, K/256 groups in K order;
+ * group bytes 0..15 are the scale codes of its 16 runs of 16 elements, bytes
+ * 16..143 its element codes, element 64c + r (c = 0..3, r = 0..63) in byte
+ * 16 + 32c + (r mod 32), low nibble for r < 32, high nibble for r >= 32.
+ * qmm_weight_bytes(N, K) is the size of N rows of groups. NaN scale codes are
+ * not supported (their weights are unspecified). */
+
+/* Host-side repack from the usual layout: elems [N][K/2] bytes with element
+ * 2i of a row in the low nibble of byte i and 2i+1 in the high nibble,
+ * scales [N][K/16] codes (scale j covers elements 16j..16j+15), into
+ * groups [N][K/256][144]. All three are host memory owned by the caller; K is
+ * a multiple of 256. Returns QMM_OK, QMM_ERR_INVALID_ARG (null pointer) or
+ * QMM_ERR_SHAPE. */
+int qmm_nvfp4_repack(const uint8_t* elems, const uint8_t* scales, int64_t N, int64_t K,
+                     uint8_t* groups);
+
+/* y = x . w^T for block-scaled FP4 weights in groups (above), on `stream`;
+ * never synchronizes. x, y, M, N, K, alignment, overlap and ownership as for
+ * qmm_run (W_groups in place of W_blocks); tensor_scale must be finite
+ * (with its internal factor 2^14), else QMM_ERR_INVALID_ARG. The weights are
+ * exact in the kernel's binary16 arithmetic; x is rounded to binary16 once,
+ * as in qmm_run. Always uses the tiled kernel. */
+int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tensor_scale,
+                  float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* Free the handle and its workspace. qmm_destroy(NULL) is a no-op returning
  * QMM_OK. The caller must make sure no work enqueued with the handle is still
  * running. */

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -127,7 +128,9 @@ int64_t resident(qmm_ctx* h, int kernel, int M, int waves, int lds) {
 
 // slots > 0: an expert-indexed call (tiled kernel only), whose grid holds up
 // to `slots` independent row groups; 0 for a plain call.
-int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slots = 0) {
+// fp4: a block-scaled FP4 call (tiled kernel, its own instantiation).
+int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slots = 0,
+              bool fp4 = false) {
   int rc = check_shape(M, N, K);
   if (rc) return rc;
   const int nb = (int)(K / 256);
@@ -140,6 +143,10 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
     if (h->forced_kernel == QMM_KERNEL_VECTOR) return QMM_ERR_INVALID_ARG;
     kernel = QMM_KERNEL_TILED;
     te = nullptr;  // table entries are for plain calls
+  }
+  if (fp4) {
+    if (h->forced_kernel == QMM_KERNEL_VECTOR) return QMM_ERR_INVALID_ARG;
+    kernel = QMM_KERNEL_TILED;  // launch shape from the table: the same group geometry
   }
   const int groups_in_grid = slots > 0 ? slots : 1;
 
@@ -189,7 +196,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   const int64_t need = (ntiles + groups - 1) / groups;
   int64_t grid = need;
   // (expert-indexed calls run their own instantiation of the tiled kernel)
-  const int64_t res = resident(h, slots > 0 ? 3 : kernel, (int)M, waves, lds);
+  const int64_t res = resident(h, fp4 ? 4 : (slots > 0 ? 3 : kernel), (int)M, waves, lds);
   if (res > 0) {
     const int64_t per_range =
         res / ((int64_t)grid_y * groups_in_grid) > 0 ? res / ((int64_t)grid_y * groups_in_grid) : 1;
@@ -380,6 +387,7 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_
   a.E = 0;
   a.expert_bytes = 0;
   a.slots = 1;
+  a.oscale = 1.0f;
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 
@@ -425,6 +433,76 @@ int qmm_run_ids(qmm_handle h, const float* x, const void* W_experts, const int32
   a.E = (int)(E < 0x7FFFFFFF ? E : 0x7FFFFFFF);
   a.expert_bytes = (long long)expert_bytes;
   a.slots = slots;
+  a.oscale = 1.0f;
+  return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+int qmm_nvfp4_repack(const uint8_t* elems, const uint8_t* scales, int64_t N, int64_t K,
+                     uint8_t* groups) {
+  if (!elems || !scales || !groups) return QMM_ERR_INVALID_ARG;
+  if (N < 1 || N > (int64_t)INT32_MAX / 32 || K < 256 || K % 256 != 0 || K > (int64_t)1 << 24)
+    return QMM_ERR_SHAPE;
+  const int64_t ng = K / 256;
+  for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* er = elems + n * (K / 2);
+    const uint8_t* sr = scales + n * (K / 16);
+    for (int64_t b = 0; b < ng; ++b) {
+      uint8_t* o = groups + (n * ng + b) * 144;
+      std::memcpy(o, sr + b * 16, 16);  // scale codes of the group's 16 runs
+      const uint8_t* eg = er + b * 128;  // the group's elements 0..255, two per byte
+      for (int c = 0; c < 4; ++c)
+        for (int r = 0; r < 32; ++r) {
+          // element 64c + r to the low nibble, 64c + 32 + r to the high nibble
+          const int lo = 64 * c + r, hi = lo + 32;
+          const uint8_t qlo = (eg[lo >> 1] >> (4 * (lo & 1))) & 0xF;
+          const uint8_t qhi = (eg[hi >> 1] >> (4 * (hi & 1))) & 0xF;
+          o[16 + 32 * c + r] = (uint8_t)(qlo | (qhi << 4));
+        }
+    }
+  }
+  return QMM_OK;
+}
+
+int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tensor_scale,
+                  float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (!h || !x || !W_groups || !y || !std::isfinite(tensor_scale * 16384.0f))
+    return QMM_ERR_INVALID_ARG;
+  int rc = check_shape(M, N, K);
+  if (rc) return rc;
+  if (((uintptr_t)x & 15) || ((uintptr_t)W_groups & 15) || ((uintptr_t)y & 3))
+    return QMM_ERR_ALIGN;
+  const size_t ybytes = (size_t)(M * N * 4);
+  if (overlaps(y, ybytes, x, (size_t)(M * K * 4)) ||
+      overlaps(y, ybytes, W_groups, (size_t)qmm_weight_bytes(N, K)))
+    return QMM_ERR_OVERLAP;
+  qmm_plan p;
+  rc = make_plan(h, M, N, K, &p, 0, true);
+  if (rc) return rc;
+  if (h->device < 0) return QMM_ERR_NO_DEVICE;
+
+  qmm::Launch a;
+  a.kernel = 4;  // the tiled kernel's FP4 instantiation
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.waves_per_wg = p.waves_per_wg;
+  a.wsplit = p.wave_splits;
+  a.grid_x = p.grid_x;
+  a.grid_y = (p.splits + p.wave_splits - 1) / p.wave_splits;
+  a.nbs = p.blocks_per_split;
+  a.xs_m = qmm::lds_xs_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.ss_m = qmm::lds_ss_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.lds_bytes = p.lds_bytes;
+  a.x = x;
+  a.W = W_groups;
+  a.y = y;
+  a.ws = h->ws;
+  a.counters = h->counters;
+  a.ids = nullptr;
+  a.E = 0;
+  a.expert_bytes = 0;
+  a.slots = 1;
+  a.oscale = tensor_scale * 16384.0f;  // the B operand carries 2^-14
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 

@@ -15,7 +15,8 @@ constexpr int kLdsMax = 160 * 1024;  // LDS a workgroup may allocate on gfx950
 constexpr int kMaxWavesPerWg = 8;
 
 struct Launch {
-  int kernel;       // 1 = row-vector, 2 = tiled (MFMA), 3 = tiled, expert-indexed
+  int kernel;       // 1 = row-vector, 2 = tiled (MFMA), 3 = tiled, expert-indexed,
+                    // 4 = tiled, block-scaled FP4 groups
   int M, N, K;
   int waves_per_wg;
   int wsplit;       // K slices reduced inside one workgroup (waves_per_wg % wsplit == 0)
@@ -36,6 +37,7 @@ struct Launch {
   int E;
   long long expert_bytes;
   int slots;
+  float oscale;     // FP4 calls: tensor scale x 2^14 applied to every output
 };
 
 // Row tiles a split-K call may have (one arrival counter each).

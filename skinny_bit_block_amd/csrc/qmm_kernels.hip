@@ -866,6 +866,75 @@ __device__ __forceinline__ void tiled_block(const BlockRegs& br, const HeaderLan
   }
 }
 
+// Block-scaled FP4 groups (qmm_run_nvfp4): 256 weights in 144 bytes like the
+// 4.5-bit super-blocks, bytes 0..15 the E4M3 scale codes of the 16 runs of 16
+// weights, bytes 16..143 the E2M1 element codes in the same byte and nibble
+// order as the 4-bit quants. Lane (r, g) reads its j-pair's four scale codes
+// (runs 4g..4g+3) with one 4-byte load and its 32 code bytes as before.
+__device__ __forceinline__ void read_block_fp4(const char* rowbuf, int g, int j, BlockRegs& b) {
+  const char* base = rowbuf + 9 * j * 16;
+  b.hd.x = *reinterpret_cast<const uint32_t*>(base + 4 * g);
+  b.qa = *reinterpret_cast<const u4_t*>(base + 16 + 32 * g);
+  b.qb = *reinterpret_cast<const u4_t*>(base + 32 + 32 * g);
+}
+
+// Two E4M3 codes (bytes 0 and 1 of p) to binary16 pairs, exactly: placing a
+// code's exponent and mantissa bits at binary16 bits 13..7 and its sign at bit
+// 15 gives its value x 2^-8 (normal and subnormal codes alike, as both formats
+// have the same structure below the exponent bias), and x 256 is exact.
+__device__ __forceinline__ h2_t e4m3_pair(uint32_t p) {
+  const uint32_t v = ((p & 0x007F007Fu) << 7) | ((p & 0x00800080u) << 8);
+  const h2_t k = {(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(h2_t, v) * k;
+}
+
+// E2M1 codes to binary16 pairs: the code's exponent and mantissa bits go to
+// binary16 bits 11..9 and its sign to bit 15, which is its value x 2^-14
+// (exponent field 0 lands as a binary16 subnormal, as in E2M1); from the
+// nibble at bits 3..0 and 19..16 of d this is ((d << 9) & 0x0E000E00) |
+// ((d << 12) & 0x80008000), and likewise for the other three nibble pairs.
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t d, int up) {
+  // up: left shift that brings the pair's nibbles to bits 3..0 and 19..16
+  const uint32_t t = up >= 0 ? d << up : d >> (-up);
+  return ((t << 9) & 0x0E000E00u) | ((t << 12) & 0x80008000u);
+}
+
+// One group for the lane's 16 rows: the B operand is code x 2^-14 x scale,
+// exact in binary16 (a multiple of 2^-24 with at most 8 significant bits), so
+// the MFMAs accumulate straight into the tile; the output scale
+// (tensor_scale x 2^14) is applied once per output.
+template <int MT>
+__device__ __forceinline__ void tiled_block_fp4(const BlockRegs& br, const char* lds_x,
+                                                const int (&xo)[MT][8], int bl, int Mx,
+                                                f4_t (&acc)[MT]) {
+  const uint32_t sc = br.hd.x;  // codes of runs 4g, 4g+1, 4g+2, 4g+3
+  const h2_t s01 = e4m3_pair(__builtin_amdgcn_perm(0u, sc, 0x0C010C00u));
+  const h2_t s23 = e4m3_pair(__builtin_amdgcn_perm(0u, sc, 0x0C030C02u));
+  const uint32_t d[8] = {br.qa.x, br.qa.y, br.qa.z, br.qa.w, br.qb.x, br.qb.y, br.qb.z, br.qb.w};
+  h8_t bw[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    // weights 64g + 4t.. use run 4g + t/4, weights 64g + 32 + 4t.. run 4g + 2 + t/4
+    const h2_t slo = t < 4 ? h2_t{s01[0], s01[0]} : h2_t{s01[1], s01[1]};
+    const h2_t shi = t < 4 ? h2_t{s23[0], s23[0]} : h2_t{s23[1], s23[1]};
+    u4_t v;
+    v.x = pk_mul(e2m1_pair(d[t], 0), slo);   // low nibbles of bytes 0, 2
+    v.y = pk_mul(e2m1_pair(d[t], -8), slo);  // low nibbles of bytes 1, 3
+    v.z = pk_mul(e2m1_pair(d[t], -4), shi);  // high nibbles of bytes 0, 2
+    v.w = pk_mul(e2m1_pair(d[t], -12), shi); // high nibbles of bytes 1, 3
+    bw[t] = __builtin_bit_cast(h8_t, v);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const char* xp = lds_x + bl * 512 * Mx;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(xp + xo[mt][t])), bw[t],
+          acc[mt], 0, 0, 0);
+  }
+}
+
 // Expert-indexed calls (ids != nullptr): row m multiplies expert ids[m] of E
 // consecutive matrices (expert_bytes apart). grid.z enumerates the distinct
 // experts in ascending order; the workgroups of slot z stream that expert's
@@ -914,7 +983,9 @@ __device__ __forceinline__ Slot make_slot(const int* __restrict__ ids, int E, lo
   return o;
 }
 
-template <int MT, bool IDS>
+// FMT 0: 4.5-bit k-quant super-blocks; FMT 1: block-scaled FP4 groups, whose
+// outputs are multiplied by oscale (the tensor scale x 2^14).
+template <int MT, bool IDS, int FMT>
 __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict__ x,
                                                         const uint8_t* __restrict__ W,
                                                         float* __restrict__ y,
@@ -923,7 +994,7 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
                                                         int N, int K, int nbs, int wsplit,
                                                         int xs_m, int ss_m,
                                                         const int* __restrict__ ids, int E,
-                                                        long long expert_bytes) {
+                                                        long long expert_bytes, float oscale) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int nb = K / kBlockWeights;
   const int waves = (int)blockDim.x >> 6;
@@ -1015,16 +1086,26 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
 #pragma unroll
         for (int j = 0; j < kStageBlocks; ++j) {
           BlockRegs br;
-          read_block(rowbuf, g, j, br);
-          tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
+          if (FMT == 1) {
+            read_block_fp4(rowbuf, g, j, br);
+            tiled_block_fp4<MT>(br, lds_x, xo, c.bl_off + bl0 + j, Mx, acc);
+          } else {
+            read_block(rowbuf, g, j, br);
+            tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
+          }
         }
       } else {
 #pragma unroll
         for (int j = 0; j < kStageBlocks; ++j) {
           if (bl0 + j < c.nbw) {
             BlockRegs br;
-            read_block(rowbuf, g, j, br);
-            tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
+            if (FMT == 1) {
+              read_block_fp4(rowbuf, g, j, br);
+              tiled_block_fp4<MT>(br, lds_x, xo, c.bl_off + bl0 + j, Mx, acc);
+            } else {
+              read_block(rowbuf, g, j, br);
+              tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
+            }
           }
         }
       }
@@ -1032,7 +1113,7 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
     if (++cs == ns) {
       float v[NV];
 #pragma unroll
-      for (int k = 0; k < NV; ++k) v[k] = acc[k >> 2][k & 3];
+      for (int k = 0; k < NV; ++k) v[k] = FMT == 1 ? acc[k >> 2][k & 3] * oscale : acc[k >> 2][k & 3];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
       finish_tile<NV>(v, mrow, grow, ok, valid, it, c, wsplit, red, r, tile * 16 + r, N, M, Mtot,
@@ -1052,17 +1133,19 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
 const void* const kVectorFn[32] = {QMM_V8(0), QMM_V8(8), QMM_V8(16), QMM_V8(24)};
 #undef QMM_V8
 #undef QMM_V
-// [expert-indexed][row tiles - 1]
-const void* const kTiledFn[2][2] = {
-    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false>),
-     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false>)},
-    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, true>),
-     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, true>)}};
+// [plain, expert-indexed, block-scaled FP4][row tiles - 1]
+const void* const kTiledFn[3][2] = {
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false, 0>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false, 0>)},
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, true, 0>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, true, 0>)},
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false, 1>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false, 1>)}};
 
 const void* kernel_fn(int kernel, int M) {
   if (M < 1 || M > 32) return nullptr;
   if (kernel == 1) return kVectorFn[M - 1];
-  if (kernel == 2 || kernel == 3) return kTiledFn[kernel == 3][M > 16 ? 1 : 0];
+  if (kernel >= 2 && kernel <= 4) return kTiledFn[kernel - 2][M > 16 ? 1 : 0];
   return nullptr;
 }
 
@@ -1073,7 +1156,7 @@ hipError_t prepare_kernels() {
     hipError_t e = hipFuncSetAttribute(kVectorFn[m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
   }
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 6; ++t) {
     hipError_t e = hipFuncSetAttribute(kTiledFn[t >> 1][t & 1],
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
@@ -1100,9 +1183,10 @@ hipError_t launch(const Launch& a, hipStream_t stream) {
   const int* ids = a.ids;
   int E = a.E;
   long long expert_bytes = a.expert_bytes;
+  float oscale = a.oscale;
   if (a.kernel != 1) {
     void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &wsplit, &xs_m, &ss_m,
-                    &ids, &E, &expert_bytes};
+                    &ids, &E, &expert_bytes, &oscale};
     return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
   }
   void* args[] = {&x, &W, &y, &ws, &counters, &N, &K, &nbs, &wsplit, &xs_m, &ss_m};
