@@ -141,8 +141,8 @@ int qmm_nvfp4_repack(const uint8_t* elems, const uint8_t* scales, int64_t N, int
 
 /* y = x . w^T for block-scaled FP4 weights in groups (above), on `stream`;
  * never synchronizes. x, y, M, N, K, alignment, overlap and ownership as for
- * qmm_run (W_groups in place of W_blocks); tensor_scale must be finite
- * (with its internal factor 2^14), else QMM_ERR_INVALID_ARG. The weights are
+ * qmm_run (W_groups in place of W_blocks); tensor_scale must be finite, else
+ * QMM_ERR_INVALID_ARG. The weights are
  * exact in the kernel's binary16 arithmetic; x is rounded to binary16 once,
  * as in qmm_run. Always uses the tiled kernel. */
 int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tensor_scale,

@@ -465,8 +465,7 @@ int qmm_nvfp4_repack(const uint8_t* elems, const uint8_t* scales, int64_t N, int
 
 int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tensor_scale,
                   float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (!h || !x || !W_groups || !y || !std::isfinite(tensor_scale * 16384.0f))
-    return QMM_ERR_INVALID_ARG;
+  if (!h || !x || !W_groups || !y || !std::isfinite(tensor_scale)) return QMM_ERR_INVALID_ARG;
   int rc = check_shape(M, N, K);
   if (rc) return rc;
   if (((uintptr_t)x & 15) || ((uintptr_t)W_groups & 15) || ((uintptr_t)y & 3))
@@ -481,7 +480,7 @@ int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tens
   if (h->device < 0) return QMM_ERR_NO_DEVICE;
 
   qmm::Launch a;
-  a.kernel = 4;  // the tiled kernel's FP4 instantiation
+  a.kernel = 4;  // the tiled kernel's FP4 instantiation (its own x staging order)
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
@@ -502,7 +501,7 @@ int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tens
   a.E = 0;
   a.expert_bytes = 0;
   a.slots = 1;
-  a.oscale = tensor_scale * 16384.0f;  // the B operand carries 2^-14
+  a.oscale = tensor_scale;
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 

@@ -298,7 +298,10 @@ __device__ __forceinline__ void x_issue(const StageArgs& a, int base, int nu, fl
 // The sub-block sums come from the same rounded values: a unit's four, then a
 // DPP sum over the eight lanes t = 0..7 of its (m, bl, g) group, which are
 // adjacent in the load order (every lane takes part; only valid units store).
-template <bool TILED, int U>
+// PAIRED (the FP4 instantiation of the tiled kernel): each dword holds x at
+// block offsets (64g + 4t + i, 64g + 32 + 4t + i), i = 0..3, the pairs the
+// hardware FP4 conversion produces from one code byte; no sub-block sums.
+template <bool TILED, int U, bool PAIRED = false>
 __device__ __forceinline__ void x_finish(const StageArgs& a, int base, int nu, float rcp,
                                          const XRegs<U>& b) {
   const int nunits = a.M * a.nbw * 32;
@@ -314,17 +317,25 @@ __device__ __forceinline__ void x_finish(const StageArgs& a, int base, int nu, f
     if (j < nu) {  // uniform
       const int u = base + j * nthr + (int)threadIdx.x;
       u4_t v;
-      v.x = cvt_pk(b.lo[j][0], b.lo[j][2]);
-      v.y = cvt_pk(b.lo[j][1], b.lo[j][3]);
-      v.z = cvt_pk(b.hi[j][0], b.hi[j][2]);
-      v.w = cvt_pk(b.hi[j][1], b.hi[j][3]);
-      const float slo = sum8(hsum2(v.x, hsum2(v.y, 0.f)));
-      const float shi = sum8(hsum2(v.z, hsum2(v.w, 0.f)));
+      float slo = 0.f, shi = 0.f;
+      if (PAIRED) {
+        v.x = cvt_pk(b.lo[j][0], b.hi[j][0]);
+        v.y = cvt_pk(b.lo[j][1], b.hi[j][1]);
+        v.z = cvt_pk(b.lo[j][2], b.hi[j][2]);
+        v.w = cvt_pk(b.lo[j][3], b.hi[j][3]);
+      } else {
+        v.x = cvt_pk(b.lo[j][0], b.lo[j][2]);
+        v.y = cvt_pk(b.lo[j][1], b.lo[j][3]);
+        v.z = cvt_pk(b.hi[j][0], b.hi[j][2]);
+        v.w = cvt_pk(b.hi[j][1], b.hi[j][3]);
+        slo = sum8(hsum2(v.x, hsum2(v.y, 0.f)));
+        shi = sum8(hsum2(v.z, hsum2(v.w, 0.f)));
+      }
       if (u < nunits) {
         if (TILED) {
           const int slot = (w.bl << lgblk) + cslot + (w.m ^ sw);
           *reinterpret_cast<u4_t*>(a.lds_x + 16 * slot) = v;
-          if (t == 0)
+          if (!PAIRED && t == 0)
             *reinterpret_cast<float2*>(a.lds_s + 2 * ((w.bl * 4 + g) * a.M + w.m)) =
                 float2{slo, shi};
         } else {
@@ -346,14 +357,14 @@ __device__ __forceinline__ void x_finish(const StageArgs& a, int base, int nu, f
 
 // Stages every chunk but the last and issues the last one's loads; returns
 // that chunk's first unit and sets nu to its units per thread.
-template <bool TILED, int U>
+template <bool TILED, int U, bool PAIRED = false>
 __device__ __forceinline__ int x_lead(const StageArgs& a, float rcp, XRegs<U>& b, int& nu) {
   const int nthr = (int)blockDim.x;
   int left = (a.M * a.nbw * 32 + nthr - 1) / nthr;
   int base = 0;
   for (; left > U; left -= U, base += U * nthr) {
     x_issue<U>(a, base, U, rcp, b);
-    x_finish<TILED, U>(a, base, U, rcp, b);
+    x_finish<TILED, U, PAIRED>(a, base, U, rcp, b);
   }
   x_issue<U>(a, base, left, rcp, b);
   nu = left;
@@ -878,7 +889,7 @@ __device__ __forceinline__ void read_block_fp4(const char* rowbuf, int g, int j,
   b.qb = *reinterpret_cast<const u4_t*>(base + 32 + 32 * g);
 }
 
-// Two E4M3 codes (bytes 0 and 1 of p) to binary16 pairs, exactly: placing a
+// Two E4M3 codes (bytes 0 and 2 of p) to a binary16 pair, exactly: placing a
 // code's exponent and mantissa bits at binary16 bits 13..7 and its sign at bit
 // 15 gives its value x 2^-8 (normal and subnormal codes alike, as both formats
 // have the same structure below the exponent bias), and x 256 is exact.
@@ -888,40 +899,33 @@ __device__ __forceinline__ h2_t e4m3_pair(uint32_t p) {
   return __builtin_bit_cast(h2_t, v) * k;
 }
 
-// E2M1 codes to binary16 pairs: the code's exponent and mantissa bits go to
-// binary16 bits 11..9 and its sign to bit 15, which is its value x 2^-14
-// (exponent field 0 lands as a binary16 subnormal, as in E2M1); from the
-// nibble at bits 3..0 and 19..16 of d this is ((d << 9) & 0x0E000E00) |
-// ((d << 12) & 0x80008000), and likewise for the other three nibble pairs.
-__device__ __forceinline__ uint32_t e2m1_pair(uint32_t d, int up) {
-  // up: left shift that brings the pair's nibbles to bits 3..0 and 19..16
-  const uint32_t t = up >= 0 ? d << up : d >> (-up);
-  return ((t << 9) & 0x0E000E00u) | ((t << 12) & 0x80008000u);
-}
-
-// One group for the lane's 16 rows: the B operand is code x 2^-14 x scale,
-// exact in binary16 (a multiple of 2^-24 with at most 8 significant bits), so
-// the MFMAs accumulate straight into the tile; the output scale
-// (tensor_scale x 2^14) is applied once per output.
+// One group for the lane's 16 rows. v_cvt_scalef32_pk_f16_fp4 turns code
+// byte i of dword t into the binary16 pair (weight 64g + 4t + i, weight
+// 64g + 32 + 4t + i), exactly (scale 1; a probe on the MI355X matched all 256
+// bytes at every byte position against the E2M1 table), and one v_pk_mul_f16
+// applies the pair's two scales (runs 4g + t/4 and 4g + 2 + t/4). The x of
+// this instantiation is staged in the same pairs (x_finish PAIRED). A product
+// of a code and a scale is exact in binary16: (8+m)*n*2^(E-4) with
+// (8+m)*n <= 180 and E >= -6, or k*n*2^-10 for subnormal scales. So the MFMAs
+// accumulate straight into the tile and the tensor scale is applied once per
+// output (oscale = the tensor scale).
 template <int MT>
 __device__ __forceinline__ void tiled_block_fp4(const BlockRegs& br, const char* lds_x,
                                                 const int (&xo)[MT][8], int bl, int Mx,
                                                 f4_t (&acc)[MT]) {
   const uint32_t sc = br.hd.x;  // codes of runs 4g, 4g+1, 4g+2, 4g+3
-  const h2_t s01 = e4m3_pair(__builtin_amdgcn_perm(0u, sc, 0x0C010C00u));
-  const h2_t s23 = e4m3_pair(__builtin_amdgcn_perm(0u, sc, 0x0C030C02u));
+  const h2_t sa = e4m3_pair(__builtin_amdgcn_perm(0u, sc, 0x0C020C00u));  // (4g, 4g+2)
+  const h2_t sb = e4m3_pair(__builtin_amdgcn_perm(0u, sc, 0x0C030C01u));  // (4g+1, 4g+3)
   const uint32_t d[8] = {br.qa.x, br.qa.y, br.qa.z, br.qa.w, br.qb.x, br.qb.y, br.qb.z, br.qb.w};
   h8_t bw[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    // weights 64g + 4t.. use run 4g + t/4, weights 64g + 32 + 4t.. run 4g + 2 + t/4
-    const h2_t slo = t < 4 ? h2_t{s01[0], s01[0]} : h2_t{s01[1], s01[1]};
-    const h2_t shi = t < 4 ? h2_t{s23[0], s23[0]} : h2_t{s23[1], s23[1]};
+    const h2_t s2 = t < 4 ? sa : sb;
     u4_t v;
-    v.x = pk_mul(e2m1_pair(d[t], 0), slo);   // low nibbles of bytes 0, 2
-    v.y = pk_mul(e2m1_pair(d[t], -8), slo);  // low nibbles of bytes 1, 3
-    v.z = pk_mul(e2m1_pair(d[t], -4), shi);  // high nibbles of bytes 0, 2
-    v.w = pk_mul(e2m1_pair(d[t], -12), shi); // high nibbles of bytes 1, 3
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[t], 1.0f, 0) * s2);
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[t], 1.0f, 1) * s2);
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[t], 1.0f, 2) * s2);
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[t], 1.0f, 3) * s2);
     bw[t] = __builtin_bit_cast(h8_t, v);
   }
 #pragma unroll
@@ -984,7 +988,7 @@ __device__ __forceinline__ Slot make_slot(const int* __restrict__ ids, int E, lo
 }
 
 // FMT 0: 4.5-bit k-quant super-blocks; FMT 1: block-scaled FP4 groups, whose
-// outputs are multiplied by oscale (the tensor scale x 2^14).
+// outputs are multiplied by oscale (the tensor scale).
 template <int MT, bool IDS, int FMT>
 __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict__ x,
                                                         const uint8_t* __restrict__ W,
@@ -1024,7 +1028,7 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   const float rcp = 1.0f / (float)M;
   XRegs<kTiledLead> xb;
   int xnu;
-  const int xbase = x_lead<true, kTiledLead>(st, rcp, xb, xnu);
+  const int xbase = x_lead<true, kTiledLead, FMT == 1>(st, rcp, xb, xnu);
   issue_barrier();
   int tile = (int)blockIdx.x * c.T + c.wtile;
   StageLane sl;
@@ -1032,7 +1036,7 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   first_stage(sl0.W, slice_base, tile, ntiles, nstages, nb, N, c.nbw, row_bytes, lane, wbuf, sl,
               sr);
   wait_vm<kStageLoads>();  // x complete; the first weight stage stays in flight
-  x_finish<true, kTiledLead>(st, xbase, xnu, rcp, xb);
+  x_finish<true, kTiledLead, FMT == 1>(st, xbase, xnu, rcp, xb);
   __syncthreads();
 
   const HeaderLane hl = header_lane(g);

@@ -49,8 +49,6 @@ def test_run_nvfp4_argument_checks():
             sbb.QMM_ERR_INVALID_ARG
         assert sbb.qmm_run_nvfp4_raw(h, 16, 16, float("inf"), 4096, 1, 16, 256, None) == \
             sbb.QMM_ERR_INVALID_ARG
-        assert sbb.qmm_run_nvfp4_raw(h, 16, 16, 3e35, 4096, 1, 16, 256, None) == \
-            sbb.QMM_ERR_INVALID_ARG
         # shape and alignment before the device check
         assert sbb.qmm_run_nvfp4_raw(h, 16, 16, 1.0, 4096, 1, 16, 300, None) == sbb.QMM_ERR_SHAPE
         assert sbb.qmm_run_nvfp4_raw(h, 8, 16, 1.0, 4096, 1, 16, 256, None) == sbb.QMM_ERR_ALIGN
