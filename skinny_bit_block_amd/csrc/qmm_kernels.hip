@@ -61,11 +61,6 @@ __device__ __forceinline__ uint32_t pk_mul(uint32_t a, h2_t s) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) * s);
 }
 
-__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
-
 __device__ __forceinline__ float f16_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
 }
@@ -214,16 +209,6 @@ __device__ __forceinline__ float hsum2(uint32_t p, float c) {
 // kernels' LDS layouts are computed from (m, bl, g, t) when storing). A probe
 // measured this order about 4x faster than reading in the tiled kernel's LDS
 // order, where each load instruction touches 64 rows-and-segments.
-struct XUnit {
-  int m, g, t, bl;
-};
-
-__device__ __forceinline__ XUnit xunit(int u, int M, float rcp) {
-  const int rest = u >> 5;
-  const int bl = div_small(rest, M, rcp);
-  return XUnit{rest - bl * M, (u >> 3) & 3, u & 7, bl};
-}
-
 // A thread's units of one chunk are base + j*nthr + threadIdx.x, j = 0, 1, ...
 // Their t and g are the thread's own (nthr is a multiple of 32); (m, bl)
 // advance by the quotient and remainder of nthr/32 by M at each step.
