@@ -132,6 +132,20 @@ def test_full_size_sampled_rows(h, M):
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("M", [1, 7])
+def test_lm_head_bench_shape_sampled_rows(h, M):
+    # the 248,320-row lm_head the FP4 bench times (the pages' FP4 bench shape)
+    N, K = 248320, 5120
+    elems, scales = synth.nvfp4(N, K, tensor=510, seed=SEED)
+    x = synth.acts(M, K, tensor=511, seed=SEED)
+    groups = sbb.qmm_nvfp4_repack(elems, scales, N, K)
+    y = run(h, x, groups, 0.5, N, K)
+    rows = np.r_[0:4, 9999:10003, N // 2:N // 2 + 4, N - 4:N]
+    yref, aref = fp4.qmm_nvfp4(x, elems, scales, 0.5, N, K, rows=rows)
+    check(y[:, rows], yref, aref, "lm_head M=%d" % M)
+    assert np.all(np.isfinite(y))
+
+
 def test_errors_launch_nothing(h):
     M, N, K = 2, 32, 256
     x = torch.zeros((M, K), dtype=torch.float32, device="cuda")
