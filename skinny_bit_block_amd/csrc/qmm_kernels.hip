@@ -39,6 +39,21 @@
 // are bit-identical from run to run for a given launch plan, and a call is a
 // single kernel launch. Each wave walks a fixed sequence of row tiles of one K
 // slice (persistent workgroups).
+//
+// The tiled kernel has two more instantiations: the expert-indexed product
+// (IDS: row m multiplies matrix ids[m]; "sixi-asi 0.9", section "The patch",
+// names the MUL_MAT_ID op) and block-scaled FP4 weights (FMT = 1: E2M1 codes
+// with one E4M3 scale per 16, repacked by the host into the same 144-byte
+// geometry, decoded with gfx950's packed FP4 conversion; FlashRT issue #153
+// measures an NVFP4 W4A16 product, the format's bits are the OCP MX / OFP8
+// specifications').
+//
+// x staging (both kernels): a workgroup loads all its x units at once (16 B of
+// binary16 each, loaded in row order so eight lanes read one 128-byte run),
+// issues its first weight stage, waits for x alone (s_waitcnt vmcnt with the
+// stage still outstanding), converts, and stores in the kernel's LDS layout;
+// the tiled layout XORs each unit's row slot with a function of its position
+// so the stores spread over all LDS banks (x_lead, x_issue, x_finish below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
