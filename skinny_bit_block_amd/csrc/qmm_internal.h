@@ -37,7 +37,7 @@ struct Launch {
   int E;
   long long expert_bytes;
   int slots;
-  float oscale;     // FP4 calls: tensor scale x 2^14 applied to every output
+  float oscale;     // FP4 calls: the tensor scale, applied to every output (1 otherwise)
 };
 
 // Row tiles a split-K call may have (one arrival counter each).
