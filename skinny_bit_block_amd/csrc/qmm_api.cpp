@@ -66,10 +66,10 @@ constexpr TableEntry kTable[] = {
     {5120, 5120, 2, QMM_KERNEL_TILED, 4, 2, 2},
     {5120, 5120, 5, QMM_KERNEL_TILED, 4, 3, 1},
     // gate+up, N = 2 x 17408
-    {34816, 5120, 1, QMM_KERNEL_VECTOR, 4, 2, 2},
-    {34816, 5120, 2, QMM_KERNEL_TILED, 4, 2, 2},
-    {34816, 5120, 4, QMM_KERNEL_TILED, 4, 1, 1},
-    {34816, 5120, 16, QMM_KERNEL_TILED, 8, 2, 1},
+    {34816, 5120, 1, QMM_KERNEL_VECTOR, 2, 2, 2},
+    {34816, 5120, 2, QMM_KERNEL_TILED, 3, 1, 1},
+    {34816, 5120, 5, QMM_KERNEL_TILED, 4, 1, 1},
+    {34816, 5120, 9, QMM_KERNEL_TILED, 8, 2, 1},
     // down
     {5120, 17408, 1, QMM_KERNEL_VECTOR, 4, 6, 2},
     {5120, 17408, 2, QMM_KERNEL_TILED, 4, 6, 2},
