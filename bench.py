@@ -7,8 +7,9 @@ M = 1, 4, 8, 16 rows. A pass is 513 calls back-to-back on one stream: per layer
 projection (5120x17408), then the 151936x5120 lm_head: 15,725,813,760 bytes of
 4.5-bit super-blocks, every matrix distinct and resident in HBM before timing.
 Prints one JSON line: weight GB/s over the step (value), ms per pass per M, the
-roofline of the dominant kernel measured live with HIP events, and the oracle
-timed on the host cores on a bounded sample as a baseline.
+same for a 32-row pass (per_m_extra, timed separately and not part of value),
+the roofline of the dominant kernel measured live with HIP events, and the
+oracle timed on the host cores on a bounded sample as a baseline.
 
 Other modes: --mode configs (per-matrix timings of the four single-matrix
 workloads with rotating copies), --mode kernels (only the per-launch kernel
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--ms", default="1,4,8,16")
+    ap.add_argument("--extra-ms", default="32",
+                    help="row counts also timed per pass but not part of value ('' for none)")
     ap.add_argument("--mode", default="pass", choices=["pass", "configs", "kernels", "copy"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -151,14 +154,16 @@ class Pass:
         return "qmm_vector_kernel<%d>" % M
 
 
-def time_passes(P, steps, warmup, graph):
-    """Per-M ms per pass, timed with HIP events on the stream the kernels run on."""
+def time_passes(P, steps, warmup, graph, ms=None):
+    """Per-M ms per pass (for the row counts ms, default all of P's), timed with
+    HIP events on the stream the kernels run on."""
     torch = P.torch
     stream = torch.cuda.current_stream()
-    ev = {M: [] for M in P.ms}
+    ms = P.ms if ms is None else ms
+    ev = {M: [] for M in ms}
 
     def one_step(record):
-        for M in P.ms:
+        for M in ms:
             if record:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -183,7 +188,7 @@ def time_passes(P, steps, warmup, graph):
     torch.cuda.synchronize()
     wall = time.time() - w0
     total_ms = t0.elapsed_time(t1)
-    per_m = {M: sum(a.elapsed_time(b) for a, b in ev[M]) / steps for M in P.ms}
+    per_m = {M: sum(a.elapsed_time(b) for a, b in ev[M]) / steps for M in ms}
     return total_ms / steps, per_m, wall
 
 
@@ -388,11 +393,12 @@ def nvfp4_measure(torch, sbb, synth, acc, h, reps=5):
 
 def mode_pass(args, torch, sbb, synth, acc):
     ms = [int(v) for v in args.ms.split(",")]
-    P = Pass(torch, sbb, synth, acc, ms, args.layers, arena=not args.separate)
+    extra = [int(v) for v in args.extra_ms.split(",") if v and int(v) not in ms]
+    P = Pass(torch, sbb, synth, acc, ms + extra, args.layers, arena=not args.separate)
     if not args.no_graph:
         P.capture()
         log("graphs captured")
-    ms_step, per_m, wall = time_passes(P, args.steps, args.warmup, graph=not args.no_graph)
+    ms_step, per_m, wall = time_passes(P, args.steps, args.warmup, graph=not args.no_graph, ms=ms)
     log("timed %d steps: %.3f ms/step (wall %.2f s)" % (args.steps, ms_step, wall))
     for M in ms:
         acc.check_roofline(P.weight_bytes, per_m[M] * 1e-3, what="pass M=%d" % M)
@@ -401,8 +407,16 @@ def mode_pass(args, torch, sbb, synth, acc):
                              "weight_gbs": round(acc.gbs(P.weight_bytes, per_m[M] * 1e-3), 1),
                              "pct_hbm_peak": round(acc.pct_of(P.weight_bytes, per_m[M] * 1e-3, 8e12), 2)}
                     for M in ms}
+    if extra:
+        _, x_per_m, _ = time_passes(P, args.steps, args.warmup, graph=not args.no_graph, ms=extra)
+        for M in extra:
+            acc.check_roofline(P.weight_bytes, x_per_m[M] * 1e-3, what="pass M=%d" % M)
+        out["per_m_extra"] = {str(M): {"ms_per_pass": round(x_per_m[M], 4),
+                                       "weight_gbs": round(acc.gbs(P.weight_bytes, x_per_m[M] * 1e-3), 1),
+                                       "pct_hbm_peak": round(acc.pct_of(P.weight_bytes, x_per_m[M] * 1e-3, 8e12), 2)}
+                              for M in extra}
     if not args.no_eager and not args.no_graph:
-        e_step, e_per_m, _ = time_passes(P, max(3, args.steps // 4), 1, graph=False)
+        e_step, e_per_m, _ = time_passes(P, max(3, args.steps // 4), 1, graph=False, ms=ms)
         out["eager"] = {str(M): {"ms_per_pass": round(e_per_m[M], 4),
                                  "weight_gbs": round(acc.gbs(P.weight_bytes, e_per_m[M] * 1e-3), 1)}
                         for M in ms}

@@ -76,6 +76,7 @@ constexpr TableEntry kTable[] = {
     {5120, 17408, 4, QMM_KERNEL_TILED, 8, 6, 2},
     {5120, 17408, 8, QMM_KERNEL_TILED, 8, 6, 1},
     {5120, 17408, 16, QMM_KERNEL_TILED, 4, 6, 1},
+    {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1},
     // lm_head
     {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1, 1},
     {151936, 5120, 2, QMM_KERNEL_TILED, 8, 1, 1},
