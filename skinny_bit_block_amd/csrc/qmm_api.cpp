@@ -59,6 +59,7 @@ int check_shape(int64_t M, int64_t N, int64_t K) {
 // points take the entry below them.
 struct TableEntry {
   int32_t N, K, m_lo, kernel, waves, splits, wsplit;
+  int32_t fmt = 0;  // 0: 4.5-bit super-blocks; 1: block-scaled FP4 groups
 };
 constexpr TableEntry kTable[] = {
     // 5120 x 5120 projections
@@ -81,13 +82,22 @@ constexpr TableEntry kTable[] = {
     {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1, 1},
     {151936, 5120, 2, QMM_KERNEL_TILED, 8, 1, 1},
     {151936, 5120, 16, QMM_KERNEL_TILED, 8, 2, 1},
+    // block-scaled FP4 gate+up (lighter dequantization: its own optimum)
+    {34816, 5120, 1, QMM_KERNEL_TILED, 3, 1, 1, 1},
+    {34816, 5120, 5, QMM_KERNEL_TILED, 6, 2, 2, 1},
+    {34816, 5120, 9, QMM_KERNEL_TILED, 6, 2, 1, 1},
 };
 
-// The entry for (M, N, K), or nullptr when the shape is not in the table.
-const TableEntry* table_entry(int64_t M, int64_t N, int64_t K) {
+// The entry for (M, N, K) and weight format fmt (the 4.5-bit entries when
+// the table has none for fmt), or nullptr when the shape is not in the table.
+const TableEntry* table_entry(int64_t M, int64_t N, int64_t K, int fmt = 0) {
   const TableEntry* best = nullptr;
-  for (const TableEntry& e : kTable)
-    if (e.N == N && e.K == K && e.m_lo <= M && (!best || e.m_lo > best->m_lo)) best = &e;
+  for (int want : {fmt, 0}) {
+    for (const TableEntry& e : kTable)
+      if (e.fmt == want && e.N == N && e.K == K && e.m_lo <= M && (!best || e.m_lo > best->m_lo))
+        best = &e;
+    if (best) break;
+  }
   return best;
 }
 
@@ -136,7 +146,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   if (rc) return rc;
   const int nb = (int)(K / 256);
   const int64_t ntiles = (N + 15) / 16;
-  const TableEntry* te = table_entry(M, N, K);
+  const TableEntry* te = table_entry(M, N, K, fp4 ? 1 : 0);
   int kernel = M >= table_switch(N, K) ? QMM_KERNEL_TILED : QMM_KERNEL_VECTOR;
   if (te) kernel = te->kernel;
   if (h->forced_kernel != QMM_KERNEL_AUTO) kernel = h->forced_kernel;

@@ -118,7 +118,7 @@ def test_repeat_is_bitwise_identical(h):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("M", [1, 7])
+@pytest.mark.parametrize("M", [1, 4, 7, 16])
 def test_full_size_sampled_rows(h, M):
     # gate+up shape, the pages' FP4 bench shape with the most rows per call
     N, K = 34816, 5120
