@@ -10,6 +10,8 @@ unpinned (no GGUF file is available to compare against).
 
 oracle.nvfp4 is the oracle of the block-scaled FP4 product (numpy, binary64;
 its header gives the format's sources and pins).
+oracle.int4 is the oracle of the plain 4-bit integer product, one binary16
+scale per 128 columns (numpy, binary64; its header gives the reading and pins).
 """
 import ctypes
 import os

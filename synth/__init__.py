@@ -55,6 +55,9 @@ def _load():
         lib.synth_nvfp4.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_nvfp4.restype = ctypes.c_int
+        lib.synth_int4.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_int4.restype = ctypes.c_int
         lib.synth_f64_to_f16.argtypes = [ctypes.c_double]
         lib.synth_f64_to_f16.restype = ctypes.c_uint16
         lib.synth_word.argtypes = [ctypes.c_uint64] * 4
@@ -110,6 +113,22 @@ def nvfp4(n_rows, K, tensor, seed=DEFAULT_SEED):
     if rc:
         raise RuntimeError("synth_nvfp4 failed")
     return elems, scales
+
+
+def int4(n_rows, K, tensor, seed=DEFAULT_SEED):
+    """Plain 4-bit integer weights in the usual two-array layout: (codes uint8
+    [n_rows, K/2], two 4-bit two's-complement codes per byte, element 2i in
+    the low nibble; scales uint16 [n_rows, K/128], binary16 bit patterns, one
+    per 128 elements). Random fields only; see synth_int4 in synth.c."""
+    if K <= 0 or K % 128:
+        raise ValueError("K must be a positive multiple of 128")
+    codes = np.empty((int(n_rows), int(K) // 2), dtype=np.uint8)
+    scales = np.empty((int(n_rows), int(K) // 128), dtype=np.uint16)
+    rc = _load().synth_int4(seed, tensor, int(n_rows), int(K), codes.ctypes.data,
+                            scales.ctypes.data)
+    if rc:
+        raise RuntimeError("synth_int4 failed")
+    return codes, scales
 
 
 def f64_to_f16_bits(v):

@@ -33,7 +33,10 @@
 
 #define SM_GAMMA 0x9E3779B97F4A7C15ULL
 
-enum { FIELD_BYTES = 1, FIELD_D = 2, FIELD_DMIN = 3, FIELD_X = 4, FIELD_FP4_ELEMS = 5, FIELD_FP4_SCALES = 6 };
+enum {
+  FIELD_BYTES = 1, FIELD_D = 2, FIELD_DMIN = 3, FIELD_X = 4, FIELD_FP4_ELEMS = 5,
+  FIELD_FP4_SCALES = 6, FIELD_INT4_CODES = 7, FIELD_INT4_SCALES = 8
+};
 
 static inline uint64_t sm_mix(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
@@ -131,6 +134,28 @@ int synth_nvfp4(uint64_t seed, uint64_t tensor, int64_t n_rows, int64_t K, uint8
     const uint64_t r = sm_word(ks, (uint64_t)i);
     scales[i] = (uint8_t)(((r % 15u) << 3) | ((r >> 8) & 7u));
   }
+  return 0;
+}
+
+/* Plain 4-bit integer weights in the usual two-array layout: codes n_rows x
+   K/2 bytes (uniform random bytes, two 4-bit codes per byte), scales n_rows x
+   K/128 binary16 bit patterns, one per 128 elements, f16_rne(|z| * 1e-2) like
+   the super-blocks' d and dmin. Only random fields: the values the codes
+   stand for are not computed here. */
+int synth_int4(uint64_t seed, uint64_t tensor, int64_t n_rows, int64_t K, uint8_t* codes,
+               uint16_t* scales) {
+  if (K <= 0 || K % 128 != 0 || n_rows < 0 || !codes || !scales) return -1;
+  const int64_t nc = n_rows * (K / 2), ns = n_rows * (K / 128);
+  const uint64_t kc = sm_key(seed, tensor, FIELD_INT4_CODES);
+  const uint64_t ks = sm_key(seed, tensor, FIELD_INT4_SCALES);
+#pragma omp parallel for schedule(static)
+  for (int64_t w = 0; w < (nc + 7) / 8; ++w) {
+    const uint64_t r = sm_word(kc, (uint64_t)w);
+    for (int t = 0; t < 8 && 8 * w + t < nc; ++t) codes[8 * w + t] = (uint8_t)(r >> (8 * t));
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < ns; ++i)
+    scales[i] = synth_f64_to_f16(fabs(sm_normal(ks, (uint64_t)i)) * 1e-2);
   return 0;
 }
 
