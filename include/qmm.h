@@ -148,6 +148,41 @@ int qmm_nvfp4_repack(const uint8_t* elems, const uint8_t* scales, int64_t N, int
 int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tensor_scale,
                   float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* Plain 4-bit integer weights, one scale per 128 columns. The "sixi-asi 0.11"
+ * page (section "What did not work") names this layout as the plain
+ * alternative to the k-quant files without fixing its bits; read here as:
+ * elements 4-bit two's-complement integers q in [-8, 7] (no zero point), one
+ * IEEE binary16 scale per 128 consecutive elements of a row;
+ * w = scale * q.
+ *
+ * The library streams them in groups of 256 weights in 144 bytes, the
+ * geometry of the 4.5-bit super-blocks: per row, K/256 groups in K order;
+ * group bytes 0..1 and 2..3 are the binary16 scales (little-endian) of its
+ * elements 0..127 and 128..255, bytes 4..15 are zero, bytes 16..143 hold the
+ * codes offset by 8 (q + 8, 0..15), element 64c + r (c = 0..3, r = 0..63) in
+ * byte 16 + 32c + (r mod 32), low nibble for r < 32, high nibble for r >= 32.
+ * The 12 padding bytes make a group 4.5 bits per weight against the layout's
+ * own 4.125; qmm_weight_bytes(N, K) is the size of N rows of groups. */
+
+/* Host-side repack from the usual layout: codes [N][K/2] bytes, element 2i
+ * of a row in the low nibble of byte i and 2i+1 in the high nibble, two's
+ * complement; scales [N][K/128] binary16 bit patterns (scale j covers
+ * elements 128j..128j+127), into groups [N][K/256][144]. All three are host
+ * memory owned by the caller; K is a multiple of 256. Returns QMM_OK,
+ * QMM_ERR_INVALID_ARG (null pointer) or QMM_ERR_SHAPE. */
+int qmm_int4_repack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                    uint8_t* groups);
+
+/* y = x . w^T for plain INT4 weights in groups (above), on `stream`; never
+ * synchronizes. x, y, M, N, K, alignment, overlap and ownership as for
+ * qmm_run (W_groups in place of W_blocks). The codes are exact in the
+ * kernel's binary16 arithmetic and the scales are applied in fp32, so zero
+ * codes give exact zeros; x is rounded to binary16 once, as in qmm_run.
+ * Infinite or NaN scales are not supported (their outputs are unspecified).
+ * Always uses the tiled kernel. */
+int qmm_run_int4(qmm_handle h, const float* x, const void* W_groups, float* y, int64_t M,
+                 int64_t N, int64_t K, hipStream_t stream);
+
 /* Free the handle and its workspace. qmm_destroy(NULL) is a no-op returning
  * QMM_OK. The caller must make sure no work enqueued with the handle is still
  * running. */

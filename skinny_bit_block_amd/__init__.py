@@ -28,7 +28,8 @@ QMM_DEVICE_NONE = -1  # planning-only handle: plans and checks arguments, never 
 KERNEL_AUTO, KERNEL_VECTOR, KERNEL_TILED = 0, 1, 2
 KERNEL_NAMES = {KERNEL_VECTOR: "vector", KERNEL_TILED: "tiled"}
 
-EXPORTS = ["qmm_create", "qmm_run", "qmm_run_ids", "qmm_run_nvfp4", "qmm_nvfp4_repack", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
+EXPORTS = ["qmm_create", "qmm_run", "qmm_run_ids", "qmm_run_nvfp4", "qmm_nvfp4_repack",
+           "qmm_run_int4", "qmm_int4_repack", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
            "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_wave_splits",
            "qmm_switch_point"]
 
@@ -65,6 +66,10 @@ def load():
         lib.qmm_run_nvfp4.restype = ctypes.c_int
         lib.qmm_nvfp4_repack.argtypes = [vp, vp, i64, i64, vp]
         lib.qmm_nvfp4_repack.restype = ctypes.c_int
+        lib.qmm_run_int4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.qmm_run_int4.restype = ctypes.c_int
+        lib.qmm_int4_repack.argtypes = [vp, vp, i64, i64, vp]
+        lib.qmm_int4_repack.restype = ctypes.c_int
         lib.qmm_destroy.argtypes = [vp]
         lib.qmm_destroy.restype = ctypes.c_int
         lib.qmm_status_string.argtypes = [ctypes.c_int]
@@ -202,10 +207,7 @@ def qmm_nvfp4_repack(elems, scales, N, K):
     return out
 
 
-def qmm_run_nvfp4(h, x, W_groups, tensor_scale, y, M, N, K, stream=None):
-    """Enqueue y = x . w^T for block-scaled FP4 weights (W_groups: uint8 device
-    tensor from qmm_nvfp4_repack) with the given fp32 tensor scale on `stream`.
-    Other arguments as for qmm_run."""
+def _check_group_args(x, W_groups, y, M, N, K):
     for name, t, dt in (("x", x, "float32"), ("W_groups", W_groups, "uint8"), ("y", y, "float32")):
         if t is not None and not isinstance(t, int):
             if not t.is_cuda:
@@ -221,8 +223,44 @@ def qmm_run_nvfp4(h, x, W_groups, tensor_scale, y, M, N, K, stream=None):
     if W_groups is not None and not isinstance(W_groups, int) and \
             W_groups.numel() < qmm_weight_bytes(N, K):
         raise ValueError("W_groups has fewer than N*K/256*144 bytes")
+
+
+def qmm_run_nvfp4(h, x, W_groups, tensor_scale, y, M, N, K, stream=None):
+    """Enqueue y = x . w^T for block-scaled FP4 weights (W_groups: uint8 device
+    tensor from qmm_nvfp4_repack) with the given fp32 tensor scale on `stream`.
+    Other arguments as for qmm_run."""
+    _check_group_args(x, W_groups, y, M, N, K)
     return _check(load().qmm_run_nvfp4(h, _ptr(x), _ptr(W_groups), float(tensor_scale), _ptr(y),
                                        int(M), int(N), int(K), _stream(stream)))
+
+
+def qmm_int4_repack(codes, scales, N, K):
+    """Plain INT4 weights from the usual layout (numpy uint8 codes [N, K/2],
+    two's complement, element 2i in the low nibble of byte i; uint16 binary16
+    scales [N, K/128]) to the library's groups: a numpy uint8 array
+    [N, K/256*144] (host memory; copy it to the device for qmm_run_int4)."""
+    import numpy as np
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if codes.size != N * K // 2 or scales.size != N * K // 128:
+        raise ValueError("codes must hold N*K/2 bytes and scales N*K/128 values")
+    out = np.empty((int(N), int(K) // 256 * 144), dtype=np.uint8)
+    _check(load().qmm_int4_repack(codes.ctypes.data, scales.ctypes.data, int(N), int(K),
+                                  out.ctypes.data))
+    return out
+
+
+def qmm_run_int4(h, x, W_groups, y, M, N, K, stream=None):
+    """Enqueue y = x . w^T for plain INT4 weights (W_groups: uint8 device tensor
+    from qmm_int4_repack) on `stream`. Other arguments as for qmm_run."""
+    _check_group_args(x, W_groups, y, M, N, K)
+    return _check(load().qmm_run_int4(h, _ptr(x), _ptr(W_groups), _ptr(y), int(M), int(N),
+                                      int(K), _stream(stream)))
+
+
+def qmm_run_int4_raw(h, x_ptr, w_ptr, y_ptr, M, N, K, stream_ptr):
+    """The C call with raw pointers; returns the status instead of raising."""
+    return load().qmm_run_int4(h, x_ptr, w_ptr, y_ptr, M, N, K, stream_ptr)
 
 
 def qmm_run_nvfp4_raw(h, x_ptr, w_ptr, tensor_scale, y_ptr, M, N, K, stream_ptr):

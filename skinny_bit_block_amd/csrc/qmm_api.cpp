@@ -139,14 +139,16 @@ int64_t resident(qmm_ctx* h, int kernel, int M, int waves, int lds) {
 
 // slots > 0: an expert-indexed call (tiled kernel only), whose grid holds up
 // to `slots` independent row groups; 0 for a plain call.
-// fp4: a block-scaled FP4 call (tiled kernel, its own instantiation).
+// fmt: 0 for 4.5-bit super-blocks; 1 a block-scaled FP4 call, 2 a plain INT4
+// call (the tiled kernel, each format its own instantiation).
 int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slots = 0,
-              bool fp4 = false) {
+              int fmt = 0) {
+  const bool groups_fmt = fmt != 0;  // both group formats run the tiled kernel
   int rc = check_shape(M, N, K);
   if (rc) return rc;
   const int nb = (int)(K / 256);
   const int64_t ntiles = (N + 15) / 16;
-  const TableEntry* te = table_entry(M, N, K, fp4 ? 1 : 0);
+  const TableEntry* te = table_entry(M, N, K, fmt);
   int kernel = M >= table_switch(N, K) ? QMM_KERNEL_TILED : QMM_KERNEL_VECTOR;
   if (te) kernel = te->kernel;
   if (h->forced_kernel != QMM_KERNEL_AUTO) kernel = h->forced_kernel;
@@ -155,11 +157,13 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
     kernel = QMM_KERNEL_TILED;
     te = nullptr;  // table entries are for plain calls
   }
-  if (fp4) {
+  if (groups_fmt) {
     if (h->forced_kernel == QMM_KERNEL_VECTOR) return QMM_ERR_INVALID_ARG;
     kernel = QMM_KERNEL_TILED;  // launch shape from the table: the same group geometry
   }
   const int groups_in_grid = slots > 0 ? slots : 1;
+  // the instantiation that runs (its LDS and residency)
+  const int kid = fmt == 1 ? 4 : (fmt == 2 ? 5 : (slots > 0 ? 3 : kernel));
 
   const int waves = h->force_waves ? h->force_waves
                                    : (te ? te->waves : (ntiles >= 4096 ? 8 : kDefaultWaves));
@@ -186,7 +190,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
     }
     splits = s_par < wsplit ? wsplit : s_par;
     while (splits < nb &&
-           qmm::lds_bytes((int)M, wsplit * ((nb + splits - 1) / splits), waves, wsplit, kernel) >
+           qmm::lds_bytes((int)M, wsplit * ((nb + splits - 1) / splits), waves, wsplit, kid) >
                qmm::kLdsMax)
       ++splits;
   }
@@ -194,7 +198,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   const int nbs = (nb + splits - 1) / splits;
   splits = (nb + nbs - 1) / nbs;  // no empty slice
   const int grid_y = (splits + wsplit - 1) / wsplit;
-  const int lds = qmm::lds_bytes((int)M, wsplit * nbs, waves, wsplit, kernel);
+  const int lds = qmm::lds_bytes((int)M, wsplit * nbs, waves, wsplit, kid);
   if (lds > qmm::kLdsMax) return QMM_ERR_INVALID_ARG;
   const int64_t ws = grid_y > 1 ? (int64_t)grid_y * M * N * 4 : 0;
   if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
@@ -206,8 +210,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   const int groups = waves / wsplit;
   const int64_t need = (ntiles + groups - 1) / groups;
   int64_t grid = need;
-  // (expert-indexed calls run their own instantiation of the tiled kernel)
-  const int64_t res = resident(h, fp4 ? 4 : (slots > 0 ? 3 : kernel), (int)M, waves, lds);
+  const int64_t res = resident(h, kid, (int)M, waves, lds);
   if (res > 0) {
     const int64_t per_range =
         res / ((int64_t)grid_y * groups_in_grid) > 0 ? res / ((int64_t)grid_y * groups_in_grid) : 1;
@@ -486,7 +489,7 @@ int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tens
       overlaps(y, ybytes, W_groups, (size_t)qmm_weight_bytes(N, K)))
     return QMM_ERR_OVERLAP;
   qmm_plan p;
-  rc = make_plan(h, M, N, K, &p, 0, true);
+  rc = make_plan(h, M, N, K, &p, 0, 1);
   if (rc) return rc;
   if (h->device < 0) return QMM_ERR_NO_DEVICE;
 
@@ -513,6 +516,79 @@ int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tens
   a.expert_bytes = 0;
   a.slots = 1;
   a.oscale = tensor_scale;
+  return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+int qmm_int4_repack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                    uint8_t* groups) {
+  if (!codes || !scales || !groups) return QMM_ERR_INVALID_ARG;
+  if (N < 1 || N > (int64_t)INT32_MAX / 32 || K < 256 || K % 256 != 0 || K > (int64_t)1 << 24)
+    return QMM_ERR_SHAPE;
+  const int64_t ng = K / 256;
+  for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* cr = codes + n * (K / 2);
+    const uint16_t* sr = scales + n * (K / 128);
+    for (int64_t b = 0; b < ng; ++b) {
+      uint8_t* o = groups + (n * ng + b) * 144;
+      std::memset(o, 0, 16);
+      for (int j = 0; j < 2; ++j) {  // scales of elements 0..127 and 128..255, little-endian
+        o[2 * j] = (uint8_t)(sr[2 * b + j] & 0xFF);
+        o[2 * j + 1] = (uint8_t)(sr[2 * b + j] >> 8);
+      }
+      const uint8_t* cg = cr + b * 128;  // the group's elements 0..255, two per byte
+      for (int c = 0; c < 4; ++c)
+        for (int r = 0; r < 32; ++r) {
+          // element 64c + r to the low nibble, 64c + 32 + r to the high nibble,
+          // each code offset by 8 (two's complement q -> q + 8)
+          const int lo = 64 * c + r, hi = lo + 32;
+          const uint8_t qlo = ((cg[lo >> 1] >> (4 * (lo & 1))) & 0xF) ^ 0x8;
+          const uint8_t qhi = ((cg[hi >> 1] >> (4 * (hi & 1))) & 0xF) ^ 0x8;
+          o[16 + 32 * c + r] = (uint8_t)(qlo | (qhi << 4));
+        }
+    }
+  }
+  return QMM_OK;
+}
+
+int qmm_run_int4(qmm_handle h, const float* x, const void* W_groups, float* y, int64_t M,
+                 int64_t N, int64_t K, hipStream_t stream) {
+  if (!h || !x || !W_groups || !y) return QMM_ERR_INVALID_ARG;
+  int rc = check_shape(M, N, K);
+  if (rc) return rc;
+  if (((uintptr_t)x & 15) || ((uintptr_t)W_groups & 15) || ((uintptr_t)y & 3))
+    return QMM_ERR_ALIGN;
+  const size_t ybytes = (size_t)(M * N * 4);
+  if (overlaps(y, ybytes, x, (size_t)(M * K * 4)) ||
+      overlaps(y, ybytes, W_groups, (size_t)qmm_weight_bytes(N, K)))
+    return QMM_ERR_OVERLAP;
+  qmm_plan p;
+  rc = make_plan(h, M, N, K, &p, 0, 2);
+  if (rc) return rc;
+  if (h->device < 0) return QMM_ERR_NO_DEVICE;
+
+  qmm::Launch a;
+  a.kernel = 5;  // the tiled kernel's INT4 instantiation
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.waves_per_wg = p.waves_per_wg;
+  a.wsplit = p.wave_splits;
+  a.grid_x = p.grid_x;
+  a.grid_y = (p.splits + p.wave_splits - 1) / p.wave_splits;
+  a.nbs = p.blocks_per_split;
+  a.xs_m = qmm::lds_xs_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.ss_m = qmm::lds_ss_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.lds_bytes = p.lds_bytes;
+  a.x = x;
+  a.W = W_groups;
+  a.y = y;
+  a.ws = h->ws;
+  a.counters = h->counters;
+  a.ids = nullptr;
+  a.E = 0;
+  a.expert_bytes = 0;
+  a.slots = 1;
+  a.oscale = 1.0f;
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 

@@ -16,7 +16,7 @@ constexpr int kMaxWavesPerWg = 8;
 
 struct Launch {
   int kernel;       // 1 = row-vector, 2 = tiled (MFMA), 3 = tiled, expert-indexed,
-                    // 4 = tiled, block-scaled FP4 groups
+                    // 4 = tiled, block-scaled FP4 groups, 5 = tiled, plain INT4 groups
   int M, N, K;
   int waves_per_wg;
   int wsplit;       // K slices reduced inside one workgroup (waves_per_wg % wsplit == 0)
@@ -65,7 +65,7 @@ __host__ __device__ inline int x_rows(int M, int kernel) {
 // LDS of a workgroup: staged x (Mx row slots), sub-block sums (M rows), then
 // (16-byte aligned) the buffer of the in-workgroup reduction when wsplit > 1
 // (two iterations' worth, 16 floats per row m, tile group and slice), then the
-// per-wave weight buffers.
+// per-wave weight buffers, then (INT4 kernel) a zero 16-byte chunk.
 __host__ __device__ inline int lds_red_base(int Mx, int M, int xs_m, int ss_m) {
   return (Mx * xs_m + M * ss_m * 4 + 15) & ~15;
 }
@@ -74,7 +74,7 @@ __host__ __device__ inline int lds_red_bytes(int M, int waves, int wsplit) {
 }
 inline int lds_bytes(int M, int nbw, int waves, int wsplit, int kernel) {
   return lds_red_base(x_rows(M, kernel), M, lds_xs_m(nbw, kernel), lds_ss_m(nbw, kernel)) +
-         lds_red_bytes(M, waves, wsplit) + waves * kWaveBufBytes;
+         lds_red_bytes(M, waves, wsplit) + waves * kWaveBufBytes + (kernel == 5 ? 16 : 0);
 }
 
 hipError_t launch(const Launch& a, hipStream_t stream);

@@ -939,6 +939,60 @@ __device__ __forceinline__ void tiled_block_fp4(const BlockRegs& br, const char*
   }
 }
 
+// Plain 4-bit integer groups (qmm_run_int4): 256 weights in 144 bytes like the
+// 4.5-bit super-blocks, bytes 0..3 the binary16 scales of weights 0..127 and
+// 128..255, bytes 16..143 the codes in the same byte and nibble order as the
+// 4-bit quants, stored offset by 8 (u = q + 8). The masks of unpack leave u as
+// binary16 subnormals u*2^-24 (low nibbles) and u*2^-20 (high nibbles); one
+// packed add (or fma with 1/16) of -8*2^-24 turns each pair into q*2^-24
+// exactly, so zero codes give exact zeros. Lane (r, g)'s j-pair lies in scale
+// group g/2, and an MFMA spans all four j-pairs, so each block runs two MFMA
+// chains: chain c reads x (A) only in the lanes of group c and a zero chunk of
+// LDS in the others (xa/xb: per-lane offsets and block strides), and the two
+// results are scaled by the row's two scales in fp32.
+template <int MT>
+__device__ __forceinline__ void tiled_block_int4(const BlockRegs& br, const char* lds,
+                                                 const uint32_t (&xa)[2][MT][8],
+                                                 const uint32_t (&xb)[2], int bl,
+                                                 f4_t (&acc)[MT]) {
+  const float s0 = f16_lo(br.hd.x) * 16777216.0f;  // 2^24: undo the code scaling
+  const float s1 = f16_hi(br.hd.x) * 16777216.0f;
+  Quants q;
+  unpack(br.qa, br.qb, q);
+  const h2_t m8 = {(_Float16)-0x1p-21f, (_Float16)-0x1p-21f};  // -8 * 2^-24
+  const h2_t r16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  h8_t bw[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u4_t v;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, q.a[t]) + m8);
+    v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, q.e[t]) + m8);
+    v.z = __builtin_bit_cast(uint32_t,
+                             __builtin_elementwise_fma(__builtin_bit_cast(h2_t, q.b[t]), r16, m8));
+    v.w = __builtin_bit_cast(uint32_t,
+                             __builtin_elementwise_fma(__builtin_bit_cast(h2_t, q.f[t]), r16, m8));
+    bw[t] = __builtin_bit_cast(h8_t, v);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    f4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t b0 = (uint32_t)bl * xb[0], b1 = (uint32_t)bl * xb[1];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u4_t a0 = *reinterpret_cast<const u4_t*>(lds + b0 + xa[0][mt][t]);
+      const u4_t a1 = *reinterpret_cast<const u4_t*>(lds + b1 + xa[1][mt][t]);
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a0), bw[t], c0, 0, 0,
+                                                  0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a1), bw[t], c1, 0, 0,
+                                                  0);
+    }
+    f4_t a = acc[mt];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = fmaf(s1, c1[i], fmaf(s0, c0[i], a[i]));
+    acc[mt] = a;
+  }
+}
+
 // Expert-indexed calls (ids != nullptr): row m multiplies expert ids[m] of E
 // consecutive matrices (expert_bytes apart). grid.z enumerates the distinct
 // experts in ascending order; the workgroups of slot z stream that expert's
@@ -1037,6 +1091,11 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
               sr);
   wait_vm<kStageLoads>();  // x complete; the first weight stage stays in flight
   x_finish<true, kTiledLead, FMT == 1>(st, xbase, xnu, rcp, xb);
+  // INT4: a zero 16-byte chunk after the wave buffers (the A operand of the
+  // lanes outside a chain's scale group)
+  const uint32_t zoff = (uint32_t)(red_base + lds_red_bytes(Mtot, waves, wsplit) +
+                                   waves * kWaveBufBytes);
+  if (FMT == 2 && threadIdx.x == 0) *reinterpret_cast<u4_t*>(lds + zoff) = u4_t{0u, 0u, 0u, 0u};
   __syncthreads();
 
   const HeaderLane hl = header_lane(g);
@@ -1053,6 +1112,20 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
 #pragma unroll
     for (int t = 0; t < 8; ++t) xo[mt][t] = 16 * ((4 * t + g) * Mx + (m ^ xswz(t, g, Mx)));
     sa[mt] = lds_s + 2 * (g * M + m);
+  }
+  // INT4: chain c's A operand is x in the lanes of scale group c (j-pairs 2c,
+  // 2c+1) and the zero chunk elsewhere: offset xa + bl * xb
+  uint32_t xa[2][MT][8], xbs[2];
+  if (FMT == 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool own = (g >> 1) == c;
+      xbs[c] = own ? (uint32_t)(512 * Mx) : 0u;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xa[c][mt][t] = own ? (uint32_t)xo[mt][t] : zoff;
+    }
   }
   const char* rowbuf = lds + wbuf + r * kBufRowStride;
   constexpr int NV = 4 * MT;  // rows m = 16 mt + 4 g + i of this lane's outputs
@@ -1093,6 +1166,9 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
           if (FMT == 1) {
             read_block_fp4(rowbuf, g, j, br);
             tiled_block_fp4<MT>(br, lds_x, xo, c.bl_off + bl0 + j, Mx, acc);
+          } else if (FMT == 2) {
+            read_block(rowbuf, g, j, br);
+            tiled_block_int4<MT>(br, lds, xa, xbs, c.bl_off + bl0 + j, acc);
           } else {
             read_block(rowbuf, g, j, br);
             tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
@@ -1106,6 +1182,9 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
             if (FMT == 1) {
               read_block_fp4(rowbuf, g, j, br);
               tiled_block_fp4<MT>(br, lds_x, xo, c.bl_off + bl0 + j, Mx, acc);
+            } else if (FMT == 2) {
+              read_block(rowbuf, g, j, br);
+              tiled_block_int4<MT>(br, lds, xa, xbs, c.bl_off + bl0 + j, acc);
             } else {
               read_block(rowbuf, g, j, br);
               tiled_block<MT>(br, hl, lds_x, xo, sa, c.bl_off + bl0 + j, M, Mx, acc);
@@ -1137,19 +1216,21 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
 const void* const kVectorFn[32] = {QMM_V8(0), QMM_V8(8), QMM_V8(16), QMM_V8(24)};
 #undef QMM_V8
 #undef QMM_V
-// [plain, expert-indexed, block-scaled FP4][row tiles - 1]
-const void* const kTiledFn[3][2] = {
+// [plain, expert-indexed, block-scaled FP4, plain INT4][row tiles - 1]
+const void* const kTiledFn[4][2] = {
     {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false, 0>),
      reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false, 0>)},
     {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, true, 0>),
      reinterpret_cast<const void*>(&qmm_tiled_kernel<2, true, 0>)},
     {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false, 1>),
-     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false, 1>)}};
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false, 1>)},
+    {reinterpret_cast<const void*>(&qmm_tiled_kernel<1, false, 2>),
+     reinterpret_cast<const void*>(&qmm_tiled_kernel<2, false, 2>)}};
 
 const void* kernel_fn(int kernel, int M) {
   if (M < 1 || M > 32) return nullptr;
   if (kernel == 1) return kVectorFn[M - 1];
-  if (kernel >= 2 && kernel <= 4) return kTiledFn[kernel - 2][M > 16 ? 1 : 0];
+  if (kernel >= 2 && kernel <= 5) return kTiledFn[kernel - 2][M > 16 ? 1 : 0];
   return nullptr;
 }
 
@@ -1160,7 +1241,7 @@ hipError_t prepare_kernels() {
     hipError_t e = hipFuncSetAttribute(kVectorFn[m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
   }
-  for (int t = 0; t < 6; ++t) {
+  for (int t = 0; t < 8; ++t) {
     hipError_t e = hipFuncSetAttribute(kTiledFn[t >> 1][t & 1],
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
