@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ids", action="store_true", help="skip the expert-indexed record")
     ap.add_argument("--no-fp4", action="store_true", help="skip the block-scaled FP4 record")
+    ap.add_argument("--no-int4", action="store_true", help="skip the plain INT4 record")
     ap.add_argument("--no-eager", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="one allocation per matrix instead of one weight arena")
@@ -391,6 +392,59 @@ def nvfp4_measure(torch, sbb, synth, acc, h, reps=5):
                         "seeded random codes, 144-byte groups", "shapes": out}
 
 
+def int4_measure(torch, sbb, synth, acc, h, reps=5):
+    """Plain INT4 product (one binary16 scale per 128 columns) on the gate+up
+    (34816x5120) and lm_head (151936x5120) shapes at 1 and 7 rows. Streamed
+    bytes are the library's 144-byte groups per 256 weights (the layout's own
+    size is 132: two scales and 128 code bytes); each timed sequence walks
+    distinct device copies (8 of gate+up, 2 of lm_head), replayed as a graph."""
+    out = {}
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda:0")
+    for name, N, K, copies in (("gate_up", 34816, 5120, 8), ("lm_head", 151936, 5120, 2)):
+        codes, scales = synth.int4(N, K, tensor=94000 + N % 1000, seed=SEED)
+        groups = torch.from_numpy(sbb.qmm_int4_repack(codes, scales, N, K).reshape(-1))
+        del codes, scales
+        Ws = [groups.to(dev) for _ in range(copies)]
+        del groups
+        wb = acc.weight_bytes(N, K)
+        res = {}
+        for M in (1, 7):
+            x = torch.from_numpy(synth.acts(M, K, tensor=95000 + M, seed=SEED)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+            def go(sp):
+                for W in Ws:
+                    rc = sbb.qmm_run_int4_raw(h, x.data_ptr(), W.data_ptr(), y.data_ptr(), M, N, K,
+                                              sp)
+                    if rc:
+                        raise RuntimeError(sbb.qmm_status_string(rc))
+
+            go(stream.cuda_stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                go(torch.cuda.current_stream().cuda_stream)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / reps / len(Ws) * 1e-3
+            acc.check_roofline(wb, t, what="int4 %s M=%d" % (name, M))
+            res[str(M)] = {"us_per_call": round(t * 1e6, 2), "weight_gbs": round(acc.gbs(wb, t), 1),
+                           "pct_hbm_peak": round(acc.pct_of(wb, t, 8e12), 2)}
+        out[name] = {"N": N, "K": K, "weight_bytes": wb, "format_bytes": N * K // 256 * 132,
+                     "per_m": res}
+        del Ws
+        torch.cuda.empty_cache()
+    return {"workload": "plain INT4 (two's-complement codes, binary16 scale per 128 columns), "
+                        "seeded random codes, 144-byte groups", "shapes": out}
+
+
 def mode_pass(args, torch, sbb, synth, acc):
     ms = [int(v) for v in args.ms.split(",")]
     extra = [int(v) for v in args.extra_ms.split(",") if v and int(v) not in ms]
@@ -442,6 +496,9 @@ def mode_pass(args, torch, sbb, synth, acc):
     if not args.no_fp4:
         log("block-scaled FP4 product...")
         out["nvfp4"] = nvfp4_measure(torch, sbb, synth, acc, P.h)
+    if not args.no_int4:
+        log("plain INT4 product...")
+        out["int4"] = int4_measure(torch, sbb, synth, acc, P.h)
     value = acc.gbs(P.weight_bytes * len(ms), ms_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

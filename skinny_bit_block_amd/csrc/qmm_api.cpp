@@ -75,8 +75,8 @@ constexpr TableEntry kTable[] = {
     {5120, 17408, 1, QMM_KERNEL_VECTOR, 4, 6, 2},
     {5120, 17408, 2, QMM_KERNEL_TILED, 4, 6, 2},
     {5120, 17408, 4, QMM_KERNEL_TILED, 8, 6, 2},
-    {5120, 17408, 8, QMM_KERNEL_TILED, 8, 6, 1},
-    {5120, 17408, 16, QMM_KERNEL_TILED, 4, 6, 1},
+    {5120, 17408, 5, QMM_KERNEL_TILED, 8, 6, 1},  // 5..8 rows stage 8 row slots of x
+    {5120, 17408, 9, QMM_KERNEL_TILED, 4, 6, 1},  // 9..16: 16 slots
     {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1},
     // lm_head
     {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1, 1},
@@ -86,6 +86,15 @@ constexpr TableEntry kTable[] = {
     {34816, 5120, 1, QMM_KERNEL_TILED, 3, 1, 1, 1},
     {34816, 5120, 5, QMM_KERNEL_TILED, 6, 2, 2, 1},
     {34816, 5120, 9, QMM_KERNEL_TILED, 6, 2, 1, 1},
+    // plain INT4 (always tiled, two MFMA chains per group); rows below an
+    // entry's first use the 4.5-bit entries
+    {5120, 5120, 1, QMM_KERNEL_TILED, 4, 2, 2, 2},
+    {5120, 5120, 9, QMM_KERNEL_TILED, 4, 3, 1, 2},
+    {34816, 5120, 5, QMM_KERNEL_TILED, 6, 2, 2, 2},
+    {34816, 5120, 9, QMM_KERNEL_TILED, 6, 2, 1, 2},
+    {5120, 17408, 5, QMM_KERNEL_TILED, 4, 3, 1, 2},
+    {5120, 17408, 9, QMM_KERNEL_TILED, 4, 6, 1, 2},
+    {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1, 2},
 };
 
 // The entry for (M, N, K) and weight format fmt (the 4.5-bit entries when

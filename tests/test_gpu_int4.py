@@ -161,6 +161,22 @@ def test_full_size_sampled_rows(h, M):
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("shape", ["square", "down", "lm_head"])
+@pytest.mark.parametrize("M", [1, 7, 16, 32])
+def test_pass_shapes_sampled_rows(h, shape, M):
+    # the other matrices of the model pass, in the launch shapes their table
+    # entries pick
+    N, K = {"square": (5120, 5120), "down": (5120, 17408), "lm_head": (151936, 5120)}[shape]
+    codes, scales = synth.int4(N, K, tensor=520 + N % 97, seed=SEED)
+    x = synth.acts(M, K, tensor=521, seed=SEED)
+    groups = sbb.qmm_int4_repack(codes, scales, N, K)
+    y = run(h, x, groups, N, K)
+    rows = np.r_[0:4, 1000:1004, N // 2:N // 2 + 4, N - 4:N]
+    yref, aref = int4.qmm_int4(x, codes, scales, N, K, rows=rows)
+    check(y[:, rows], yref, aref, "%s M=%d" % (shape, M))
+    assert np.all(np.isfinite(y))
+
+
 def test_errors_launch_nothing(h):
     M, N, K = 2, 32, 256
     x = torch.zeros((M, K), dtype=torch.float32, device="cuda")

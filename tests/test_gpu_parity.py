@@ -170,7 +170,7 @@ def test_gate_up(h, M):
     check(y[:, rows], yref, aref, "gate+up M=%d" % M)
 
 
-@pytest.mark.parametrize("M", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("M", [1, 4, 6, 8, 12, 16, 32])
 def test_down(h, M):
     N, K = 5120, 17408
     x, W = inputs(M, N, K, tag=2, xscale=0.1)
