@@ -40,13 +40,15 @@
 // single kernel launch. Each wave walks a fixed sequence of row tiles of one K
 // slice (persistent workgroups).
 //
-// The tiled kernel has two more instantiations: the expert-indexed product
+// The tiled kernel has three more instantiations: the expert-indexed product
 // (IDS: row m multiplies matrix ids[m]; "sixi-asi 0.9", section "The patch",
-// names the MUL_MAT_ID op) and block-scaled FP4 weights (FMT = 1: E2M1 codes
+// names the MUL_MAT_ID op), block-scaled FP4 weights (FMT = 1: E2M1 codes
 // with one E4M3 scale per 16, repacked by the host into the same 144-byte
 // geometry, decoded with gfx950's packed FP4 conversion; FlashRT issue #153
 // measures an NVFP4 W4A16 product, the format's bits are the OCP MX / OFP8
-// specifications').
+// specifications') and plain INT4 weights (FMT = 2: two's-complement codes
+// with one binary16 scale per 128 columns, "sixi-asi 0.11", section "What
+// did not work"; same geometry, exact code decode, two MFMA chains per group).
 //
 // x staging (both kernels): a workgroup loads all its x units at once (16 B of
 // binary16 each, loaded in row order so eight lanes read one 128-byte run),
