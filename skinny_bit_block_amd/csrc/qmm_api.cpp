@@ -59,7 +59,9 @@ int check_shape(int64_t M, int64_t N, int64_t K) {
 // points take the entry below them.
 struct TableEntry {
   int32_t N, K, m_lo, kernel, waves, splits, wsplit;
-  int32_t fmt = 0;  // 0: 4.5-bit super-blocks; 1: block-scaled FP4 groups
+  int32_t fmt = 0;  // 0: 4.5-bit super-blocks; 1: block-scaled FP4 groups; 2: plain INT4
+  int32_t one_tile = 0;  // 1: a workgroup per tile group (no residency cap; the
+                         // dispatcher balances the tail)
 };
 constexpr TableEntry kTable[] = {
     // 5120 x 5120 projections
@@ -76,7 +78,7 @@ constexpr TableEntry kTable[] = {
     {5120, 17408, 2, QMM_KERNEL_TILED, 4, 6, 2},
     {5120, 17408, 4, QMM_KERNEL_TILED, 8, 6, 2},
     {5120, 17408, 5, QMM_KERNEL_TILED, 8, 6, 1},  // 5..8 rows stage 8 row slots of x
-    {5120, 17408, 9, QMM_KERNEL_TILED, 4, 6, 1},  // 9..16: 16 slots
+    {5120, 17408, 9, QMM_KERNEL_TILED, 4, 6, 1, 0, 1},  // 9..16: 16 slots
     {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1},
     // lm_head
     {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1, 1},
@@ -219,7 +221,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   const int groups = waves / wsplit;
   const int64_t need = (ntiles + groups - 1) / groups;
   int64_t grid = need;
-  const int64_t res = resident(h, kid, (int)M, waves, lds);
+  const int64_t res = (te && te->one_tile) ? 0 : resident(h, kid, (int)M, waves, lds);
   if (res > 0) {
     const int64_t per_range =
         res / ((int64_t)grid_y * groups_in_grid) > 0 ? res / ((int64_t)grid_y * groups_in_grid) : 1;
