@@ -65,14 +65,15 @@ struct TableEntry {
 };
 constexpr TableEntry kTable[] = {
     // 5120 x 5120 projections
-    {5120, 5120, 1, QMM_KERNEL_VECTOR, 4, 5, 2},
+    {5120, 5120, 1, QMM_KERNEL_VECTOR, 4, 2, 2},
     {5120, 5120, 2, QMM_KERNEL_TILED, 4, 2, 2},
     {5120, 5120, 5, QMM_KERNEL_TILED, 4, 3, 1},
     // gate+up, N = 2 x 17408
     {34816, 5120, 1, QMM_KERNEL_VECTOR, 2, 2, 2},
     {34816, 5120, 2, QMM_KERNEL_TILED, 3, 1, 1},
-    {34816, 5120, 5, QMM_KERNEL_TILED, 4, 1, 1},
-    {34816, 5120, 9, QMM_KERNEL_TILED, 8, 2, 1},
+    {34816, 5120, 5, QMM_KERNEL_TILED, 6, 2, 2},
+    {34816, 5120, 9, QMM_KERNEL_TILED, 6, 2, 1},
+    {34816, 5120, 17, QMM_KERNEL_TILED, 8, 4, 1},
     // down
     {5120, 17408, 1, QMM_KERNEL_VECTOR, 4, 6, 2},
     {5120, 17408, 2, QMM_KERNEL_TILED, 4, 6, 2},
@@ -81,7 +82,7 @@ constexpr TableEntry kTable[] = {
     {5120, 17408, 9, QMM_KERNEL_TILED, 4, 6, 1, 0, 1},  // 9..16: 16 slots
     {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1},
     // lm_head
-    {151936, 5120, 1, QMM_KERNEL_VECTOR, 4, 1, 1},
+    {151936, 5120, 1, QMM_KERNEL_VECTOR, 8, 1, 1},
     {151936, 5120, 2, QMM_KERNEL_TILED, 8, 1, 1},
     {151936, 5120, 16, QMM_KERNEL_TILED, 8, 2, 1},
     // block-scaled FP4 gate+up (lighter dequantization: its own optimum)
