@@ -177,8 +177,11 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   // the instantiation that runs (its LDS and residency)
   const int kid = fmt == 1 ? 4 : (fmt == 2 ? 5 : (slots > 0 ? 3 : kernel));
 
+  // without a table entry: 8 waves from 4096 row tiles of work in the grid
+  // (an expert-indexed call streams one matrix per slot)
   const int waves = h->force_waves ? h->force_waves
-                                   : (te ? te->waves : (ntiles >= 4096 ? 8 : kDefaultWaves));
+                                   : (te ? te->waves
+                                         : (ntiles * groups_in_grid >= 4096 ? 8 : kDefaultWaves));
   if (waves < 1 || waves > qmm::kMaxWavesPerWg) return QMM_ERR_INVALID_ARG;
   int wsplit = h->force_wsplit ? h->force_wsplit : (te ? te->wsplit : 1);
   if (!h->force_wsplit && waves % wsplit) wsplit = 1;
