@@ -81,6 +81,8 @@ constexpr TableEntry kTable[] = {
     {5120, 17408, 5, QMM_KERNEL_TILED, 8, 6, 1},  // 5..8 rows stage 8 row slots of x
     {5120, 17408, 9, QMM_KERNEL_TILED, 4, 6, 1, 0, 1},  // 9..16: 16 slots
     {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1},
+    // single 2048 x 2048 projection (4 rows): every slice in one workgroup
+    {2048, 2048, 4, QMM_KERNEL_TILED, 4, 4, 4},
     // lm_head
     {151936, 5120, 1, QMM_KERNEL_VECTOR, 8, 1, 1},
     {151936, 5120, 2, QMM_KERNEL_TILED, 8, 1, 1},
@@ -184,7 +186,9 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
                                          : (ntiles * groups_in_grid >= 4096 ? 8 : kDefaultWaves));
   if (waves < 1 || waves > qmm::kMaxWavesPerWg) return QMM_ERR_INVALID_ARG;
   int wsplit = h->force_wsplit ? h->force_wsplit : (te ? te->wsplit : 1);
-  if (!h->force_wsplit && waves % wsplit) wsplit = 1;
+  // a table split that does not fit forced waves or slices falls back to 1
+  if (!h->force_wsplit && (waves % wsplit || (h->force_splits && h->force_splits < wsplit)))
+    wsplit = 1;
   if (wsplit < 1 || waves % wsplit) return QMM_ERR_INVALID_ARG;
 
   // K slices: the table's count, or enough tile-slices to fill the chip while
