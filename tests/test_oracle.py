@@ -232,3 +232,30 @@ def test_rejects_bad_shapes():
         oracle.qmm(np.zeros((1, 300), np.float32), W, 2, 300)
     with pytest.raises(ValueError):
         oracle.qmm_rows(np.zeros((1, 512), np.float32), W, 2, 512, [2])
+
+
+@pytest.mark.parametrize("N,K,rows", [
+    (5, 512, [4, 0, 2, 2, 4, 1]),        # out of order, repeated, last row
+    (3, 768, [2, 2, 1, 0]),
+    (7, 256, [6, 3, 6, 0, 5, 1, 2, 4]),
+])
+def test_dequant_rows_match_exact_decoder(N, K, rows):
+    # the read-out reference of the GPU one-hot probes: each requested row,
+    # in the requested order, equals the exact rational decode of that row of
+    # the packed matrix (an independent decoder); a wrong row or block offset
+    # would pick up another row's bytes
+    W = synth.weights(N, K, tensor=321 + N, seed=20261202)
+    exact = exact_ref.matrix_weights(W.reshape(-1), N, K)
+    got = oracle.dequant_rows(W, N, K, np.array(rows))
+    assert got.shape == (len(rows), K)
+    for i, r in enumerate(rows):
+        assert [Fraction(v) for v in got[i]] == exact[r], (r, i)
+    # distinct rows really differ, so the check above can tell rows apart
+    assert not np.array_equal(got[0], oracle.dequant_rows(W, N, K, np.array([rows[0] - 1]))[0])
+
+
+def test_dequant_rows_rejects_bad_rows():
+    W = synth.weights(4, 256, tensor=9, seed=20261202)
+    for bad in ([4], [-1]):
+        with pytest.raises(ValueError):
+            oracle.dequant_rows(W, 4, 256, np.array(bad))
