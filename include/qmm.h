@@ -61,7 +61,8 @@ enum {
   QMM_ERR_NO_DEVICE = -4,   /* device index invalid or not gfx950 */
   QMM_ERR_OOM = -5,         /* workspace allocation failed in qmm_create */
   QMM_ERR_HIP = -6,         /* a HIP runtime call or a launch failed */
-  QMM_ERR_OVERLAP = -7      /* y overlaps x or W_blocks */
+  QMM_ERR_OVERLAP = -7,     /* y overlaps x or W_blocks */
+  QMM_ERR_SCRATCH = -8      /* qmm_run_static: the plan needs more scratch than it has */
 };
 
 /* Largest batch (rows of x) a call accepts: one row per stream for up to 32
@@ -182,6 +183,26 @@ int qmm_int4_repack(const uint8_t* codes, const uint16_t* scales, int64_t N, int
  * Always uses the tiled kernel. */
 int qmm_run_int4(qmm_handle h, const float* x, const void* W_groups, float* y, int64_t M,
                  int64_t N, int64_t K, hipStream_t stream);
+
+/* y = x . dequant(W_blocks)^T like qmm_run, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc. It takes no handle and calls no
+ * allocating routine. Its split-K workspace is a static device array of the
+ * library (32 MiB of partial sums and 65536 row-tile counters, 33 MiB per
+ * device, held by each device the library runs on until the process ends),
+ * set up at the first call on a device (that call also enqueues a small
+ * kernel on `stream` that zeroes the counters). It runs on the current HIP
+ * device, plans like a fresh handle (the launch table, no overrides) and
+ * launches the same kernels, so it gives the same bits as qmm_run with the
+ * same plan. A call whose plan needs more split-K workspace than the array
+ * holds (e.g. a 151936-row matrix at more than 16 rows) returns
+ * QMM_ERR_SCRATCH and launches nothing. Every call on one device shares that
+ * device's array, so calls that overlap in time on one device (several
+ * streams, or host threads) race on it and must be serialized by the caller.
+ * Arguments, layouts, ownership, alignment and the other status codes are
+ * those of qmm_run. */
+int qmm_run_static(const float* x, const void* W_blocks, float* y, int64_t M, int64_t N,
+                   int64_t K, hipStream_t stream);
 
 /* Free the handle and its workspace. qmm_destroy(NULL) is a no-op returning
  * QMM_OK. The caller must make sure no work enqueued with the handle is still

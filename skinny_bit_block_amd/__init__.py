@@ -22,13 +22,14 @@ QMM_ERR_NO_DEVICE = -4
 QMM_ERR_OOM = -5
 QMM_ERR_HIP = -6
 QMM_ERR_OVERLAP = -7
+QMM_ERR_SCRATCH = -8
 QMM_MAX_M = 32
 QMM_DEVICE_NONE = -1  # planning-only handle: plans and checks arguments, never launches
 
 KERNEL_AUTO, KERNEL_VECTOR, KERNEL_TILED = 0, 1, 2
 KERNEL_NAMES = {KERNEL_VECTOR: "vector", KERNEL_TILED: "tiled"}
 
-EXPORTS = ["qmm_create", "qmm_run", "qmm_run_ids", "qmm_run_nvfp4", "qmm_nvfp4_repack",
+EXPORTS = ["qmm_create", "qmm_run", "qmm_run_static", "qmm_run_ids", "qmm_run_nvfp4", "qmm_nvfp4_repack",
            "qmm_run_int4", "qmm_int4_repack", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
            "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_wave_splits",
            "qmm_switch_point"]
@@ -60,6 +61,8 @@ def load():
         lib.qmm_create.restype = ctypes.c_int
         lib.qmm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         lib.qmm_run.restype = ctypes.c_int
+        lib.qmm_run_static.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        lib.qmm_run_static.restype = ctypes.c_int
         lib.qmm_run_ids.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, i64, vp]
         lib.qmm_run_ids.restype = ctypes.c_int
         lib.qmm_run_nvfp4.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i64, i64, vp]
@@ -160,6 +163,21 @@ def qmm_run(h, x, W_blocks, y, M, N, K, stream=None):
         raise ValueError("W_blocks has fewer than N*K/256*144 bytes")
     return _check(load().qmm_run(h, _ptr(x), _ptr(W_blocks), _ptr(y), int(M), int(N), int(K),
                                  _stream(stream)))
+
+
+def qmm_run_static(x, W_blocks, y, M, N, K, stream=None):
+    """qmm_run without a handle and without allocating: the library's static
+    per-device scratch serves as split-K workspace (QMM_ERR_SCRATCH when the
+    call's plan needs more). Runs on the current device; arguments as for
+    qmm_run."""
+    _check_group_args(x, W_blocks, y, M, N, K)
+    return _check(load().qmm_run_static(_ptr(x), _ptr(W_blocks), _ptr(y), int(M), int(N), int(K),
+                                        _stream(stream)))
+
+
+def qmm_run_static_raw(x_ptr, w_ptr, y_ptr, M, N, K, stream_ptr):
+    """The C call with raw pointers; returns the status instead of raising."""
+    return int(load().qmm_run_static(x_ptr, w_ptr, y_ptr, int(M), int(N), int(K), stream_ptr))
 
 
 def qmm_run_ids(h, x, W_experts, ids, E, y, M, N, K, stream=None):

@@ -13,6 +13,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/qmm.h"
@@ -33,6 +34,8 @@ struct qmm_ctx {
   float* ws;            // split-K partials
   int64_t ws_bytes;
   unsigned* counters;   // split-K arrival counters, one per row tile, zeroed at creation
+  int64_t max_counter_tiles;  // row tiles the counters cover
+  bool fixed_scratch;   // the static scratch: a plan that does not fit is QMM_ERR_SCRATCH
 };
 
 namespace {
@@ -204,7 +207,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
       s_par = te->splits < nb ? te->splits : nb;
     } else {
       while (ntiles * s_par < kTargetTiles && (nb + s_par) / (s_par + 1) >= kMinBlocksPerSlice &&
-             ntiles <= qmm::kMaxCounterTiles)
+             ntiles <= h->max_counter_tiles)
         ++s_par;
     }
     splits = s_par < wsplit ? wsplit : s_par;
@@ -220,8 +223,9 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   const int lds = qmm::lds_bytes((int)M, wsplit * nbs, waves, wsplit, kid);
   if (lds > qmm::kLdsMax) return QMM_ERR_INVALID_ARG;
   const int64_t ws = grid_y > 1 ? (int64_t)grid_y * M * N * 4 : 0;
-  if (ws > h->ws_bytes) return QMM_ERR_INVALID_ARG;
-  if (grid_y > 1 && ntiles * groups_in_grid > qmm::kMaxCounterTiles) return QMM_ERR_INVALID_ARG;
+  const int too_big = h->fixed_scratch ? QMM_ERR_SCRATCH : QMM_ERR_INVALID_ARG;
+  if (ws > h->ws_bytes) return too_big;
+  if (grid_y > 1 && ntiles * groups_in_grid > h->max_counter_tiles) return too_big;
 
   // at most one row tile per tile group of wsplit waves, and no more
   // workgroups than the device holds at once: the waves then walk several
@@ -268,6 +272,7 @@ const char* qmm_status_string(int status) {
     case QMM_ERR_OOM: return "QMM_ERR_OOM: workspace allocation failed";
     case QMM_ERR_HIP: return "QMM_ERR_HIP: a HIP runtime call or kernel launch failed";
     case QMM_ERR_OVERLAP: return "QMM_ERR_OVERLAP: y overlaps x or W_blocks";
+    case QMM_ERR_SCRATCH: return "QMM_ERR_SCRATCH: the call's split-K plan needs more than the static scratch holds (32 MiB of partial sums, 65536 row tiles); use qmm_run";
     default: return "QMM: unknown status";
   }
 }
@@ -288,6 +293,8 @@ int qmm_create(qmm_handle* out, int device) {
   h->ws = nullptr;
   h->ws_bytes = kWorkspaceBytes;
   h->counters = nullptr;
+  h->max_counter_tiles = qmm::kMaxCounterTiles;
+  h->fixed_scratch = false;
   h->nocc = 0;
   if (device == -1) {  // planning-only handle
     *out = h;
@@ -600,6 +607,89 @@ int qmm_run_int4(qmm_handle h, const float* x, const void* W_groups, float* y, i
   a.lds_bytes = p.lds_bytes;
   a.x = x;
   a.W = W_groups;
+  a.y = y;
+  a.ws = h->ws;
+  a.counters = h->counters;
+  a.ids = nullptr;
+  a.E = 0;
+  a.expert_bytes = 0;
+  a.slots = 1;
+  a.oscale = 1.0f;
+  return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+// The entry point that allocates nothing. Its context lives in a static
+// table (one per device, set up at the first call on that device): the
+// device's properties, the occupancy cache, and the static scratch of the
+// kernel file as workspace.
+namespace {
+constexpr int kMaxStaticCtx = 64;
+std::mutex g_static_mu;
+qmm_ctx g_static_ctx[kMaxStaticCtx];
+bool g_static_ready[kMaxStaticCtx];
+}  // namespace
+
+int qmm_run_static(const float* x, const void* W_blocks, float* y, int64_t M, int64_t N,
+                   int64_t K, hipStream_t stream) {
+  if (!x || !W_blocks || !y) return QMM_ERR_INVALID_ARG;
+  int rc = check_shape(M, N, K);
+  if (rc) return rc;
+  if (((uintptr_t)x & 15) || ((uintptr_t)W_blocks & 15) || ((uintptr_t)y & 3))
+    return QMM_ERR_ALIGN;
+  const size_t ybytes = (size_t)(M * N * 4);
+  if (overlaps(y, ybytes, x, (size_t)(M * K * 4)) ||
+      overlaps(y, ybytes, W_blocks, (size_t)qmm_weight_bytes(N, K)))
+    return QMM_ERR_OVERLAP;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kMaxStaticCtx)
+    return QMM_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  qmm_ctx* h = &g_static_ctx[device];
+  if (!g_static_ready[device]) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess ||
+        std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return QMM_ERR_NO_DEVICE;
+    void* scratch = nullptr;
+    if (qmm::static_scratch(device, &scratch) != hipSuccess || qmm::prepare_kernels() != hipSuccess) {
+      (void)hipGetLastError();
+      return QMM_ERR_HIP;
+    }
+    h->device = device;
+    h->cus = prop.multiProcessorCount;
+    h->nocc = 0;
+    h->forced_kernel = QMM_KERNEL_AUTO;
+    h->force_waves = h->force_splits = h->force_grid = h->force_wsplit = 0;
+    h->ws = static_cast<float*>(scratch);
+    h->ws_bytes = (int64_t)qmm::kStaticPartialBytes;
+    h->counters = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(scratch) +
+                                              qmm::kStaticPartialBytes);
+    h->max_counter_tiles = qmm::kStaticCounterTiles;
+    h->fixed_scratch = true;
+    // the counters start at zero (and every split-K call leaves them so):
+    // cleared once, on the caller's stream, ahead of the first launch
+    if (qmm::clear_counters(h->counters, qmm::kStaticCounterTiles, stream) != hipSuccess)
+      return QMM_ERR_HIP;
+    g_static_ready[device] = true;
+  }
+  qmm_plan p;
+  rc = make_plan(h, M, N, K, &p);
+  if (rc) return rc;
+  qmm::Launch a;
+  a.kernel = p.kernel;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.waves_per_wg = p.waves_per_wg;
+  a.wsplit = p.wave_splits;
+  a.grid_x = p.grid_x;
+  a.grid_y = (p.splits + p.wave_splits - 1) / p.wave_splits;
+  a.nbs = p.blocks_per_split;
+  a.xs_m = qmm::lds_xs_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.ss_m = qmm::lds_ss_m(p.wave_splits * p.blocks_per_split, p.kernel);
+  a.lds_bytes = p.lds_bytes;
+  a.x = x;
+  a.W = W_blocks;
   a.y = y;
   a.ws = h->ws;
   a.counters = h->counters;

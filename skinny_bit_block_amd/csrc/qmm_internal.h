@@ -77,6 +77,17 @@ inline int lds_bytes(int M, int nbw, int waves, int wsplit, int kernel) {
          lds_red_bytes(M, waves, wsplit) + waves * kWaveBufBytes + (kernel == 5 ? 16 : 0);
 }
 
+// The static scratch of the allocation-free entry point: kStaticPartialBytes
+// of split-K partials followed by kStaticCounterTiles arrival counters.
+constexpr size_t kStaticPartialBytes = (size_t)32 << 20;
+constexpr int kStaticCounterTiles = 1 << 16;
+// Device address of that array on `device`, which must be the current device
+// (resolved once per device with hipGetSymbolAddress, then cached).
+hipError_t static_scratch(int device, void** out);
+// Zero n counters with a fill kernel on `stream` (no memset node, so the call
+// may be captured into a graph).
+hipError_t clear_counters(unsigned* counters, int n, hipStream_t stream);
+
 hipError_t launch(const Launch& a, hipStream_t stream);
 hipError_t prepare_kernels();  // raise the dynamic-LDS limit of every kernel
 // Workgroups of the kernel a launch with these parameters uses that one

@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -1236,7 +1238,44 @@ const void* kernel_fn(int kernel, int M) {
   return nullptr;
 }
 
+// Scratch of the entry point that allocates nothing (qmm_run_static): the
+// split-K partial sums, then one 32-bit arrival counter per row tile, in one
+// file-scope device array. Every device the library runs on holds its own
+// copy until the process ends. Host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol): static_scratch()
+// resolves the device address once per device and every launch uses that.
+static __device__ __align__(256) unsigned char scratch[kStaticPartialBytes + kStaticCounterTiles * 4];
+
+__global__ void zero_u32(unsigned* __restrict__ p, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxStaticDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxStaticDevices];
+
 }  // namespace
+
+hipError_t static_scratch(int device, void** out) {
+  if (device < 0 || device >= kMaxStaticDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));  // current device
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+hipError_t clear_counters(unsigned* counters, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32, dim3((n + 255) / 256), dim3(256), 0, stream, counters, n);
+  return hipGetLastError();
+}
 
 hipError_t prepare_kernels() {
   for (int m = 0; m < 32; ++m) {
