@@ -6,15 +6,23 @@ M = 1, 4, 8, 16 rows. A pass is 513 calls back-to-back on one stream: per layer
 (64) six 5120x5120 projections, the fused gate+up (34816x5120) and the down
 projection (5120x17408), then the 151936x5120 lm_head: 15,725,813,760 bytes of
 4.5-bit super-blocks, every matrix distinct and resident in HBM before timing.
-Prints one JSON line: weight GB/s over the step (value), ms per pass per M, the
-same for a 32-row pass (per_m_extra, timed separately and not part of value),
-the roofline of the dominant kernel measured live with HIP events, and the
-oracle timed on the host cores on a bounded sample as a baseline.
+Prints one JSON line: weight GB/s over the step (value), ms per pass per M, and
+in the same run: the 32-row pass, a fused-projection pass (each layer's five
+same-input projections as one 25600-row call: 257 calls over the same bytes),
+the four single-matrix workloads per row count, the memory-system probes
+(stream-read ceiling, sustained read, launch gap), per-(shape, M) kernel
+durations, the roofline of the dominant kernel and the oracle timed on the
+host cores on a bounded sample.
 
-Other modes: --mode configs (per-matrix timings of the four single-matrix
-workloads with rotating copies), --mode kernels (only the per-launch kernel
-timing region, for rocprofv3 runs), --mode copy (a plain device copy of known
-size, the calibration of the FETCH_SIZE / WRITE_SIZE counters).
+Kernel durations are the kernels' own execution times: every timed launch
+records HIP events at the start and end of the kernel itself (the library's
+qmm_set_launch_events hook), which is what rocprofv3's kernel trace measures.
+
+Other modes: --mode configs (the single-matrix workloads only), --mode kernels
+(only the event-timed eager launches, for rocprofv3 runs; --seq-out writes
+the launch sequence that skinny_bit_block_amd/profile_summary.py maps the
+trace onto), --mode copy (a plain device copy of known size, the
+calibration of the FETCH_SIZE / WRITE_SIZE counters).
 """
 import argparse
 import ctypes
@@ -57,45 +65,66 @@ def parse():
     ap.add_argument("--no-fp4", action="store_true", help="skip the block-scaled FP4 record")
     ap.add_argument("--no-int4", action="store_true", help="skip the plain INT4 record")
     ap.add_argument("--no-eager", action="store_true")
-    ap.add_argument("--separate", action="store_true",
-                    help="one allocation per matrix instead of one weight arena")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-projection pass")
+    ap.add_argument("--no-configs", action="store_true", help="skip the single-matrix workloads")
+    ap.add_argument("--no-probes", action="store_true", help="skip the memory-system probes")
+    ap.add_argument("--seq-out", default="", help="--mode kernels: write the launch sequence here")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--layers", type=int, default=64, help="(for quick tests only; the metric needs 64)")
     return ap.parse_args()
 
 
-class Pass:
-    """Device-resident weights, activations and outputs of one full model pass."""
+# the single-matrix workloads: (name, N, K, row counts, activation scale)
+CONFIGS = [("single 2048x2048", 2048, 2048, [4], 1.0),
+           ("gate+up 34816x5120", 34816, 5120, [1, 2, 4, 7, 8, 9, 16], 1.0),
+           ("down 5120x17408", 5120, 17408, [1, 4, 8, 16], 0.1),
+           ("lm_head 151936x5120", 151936, 5120, [1, 7], 1.0)]
 
-    def __init__(self, torch, sbb, synth, acc, ms, layers, arena=True):
+
+def shape_class(N, K):
+    return {(5120, 5120): "square", (34816, 5120): "gate_up", (5120, 17408): "down",
+            (151936, 5120): "lm_head", (25600, 5120): "fused_5x5120", (2048, 2048): "single_2048"}.get(
+        (N, K), "%dx%d" % (N, K))
+
+
+class Pass:
+    """Device-resident weights, activations and outputs of one full model pass.
+
+    The arena holds each layer's six 5120x5120 projections back to back, then
+    its gate+up and down projection (each at a 2 MiB-aligned start), then the
+    lm_head, the way an inference engine keeps its weights. The first five
+    projections of a layer therefore also form one contiguous 25600x5120
+    matrix: the fused-projection pass calls that once (they share one input in
+    the layer) and the sixth separately, over exactly the same bytes.
+    """
+
+    def __init__(self, torch, sbb, synth, acc, ms, layers):
+        import numpy as np
         self.torch, self.sbb = torch, sbb
         self.shapes = [s for s in acc.full_pass_shapes()
                        if s[0] == "lm_head" or int(s[0][1:].split(".")[0]) < layers]
         self.weight_bytes = sum(acc.weight_bytes(N, K) for _, N, K in self.shapes)
         self.ms = ms
         dev = torch.device("cuda:0")
+        align = 2 << 20
+        offs, total = [], 0
+        for i, (name, N, K) in enumerate(self.shapes):
+            contiguous = ".proj" in name and not name.endswith(".proj0")
+            if not contiguous:
+                total = -(-total // align) * align
+            offs.append(total)
+            total += acc.weight_bytes(N, K)
+        self.arena = torch.empty(-(-total // align) * align, dtype=torch.uint8, device=dev)
         self.W = []
         bufs = {}
         t0 = time.time()
-        # all matrices in one device allocation, each at a 2 MiB-aligned offset
-        # (the way an inference engine keeps its weights)
-        align = 2 << 20
-        offs, total = [], 0
-        for _, N, K in self.shapes:
-            offs.append(total)
-            total += -(-acc.weight_bytes(N, K) // align) * align
-        self.arena = torch.empty(total, dtype=torch.uint8, device=dev) if arena else None
         for i, (name, N, K) in enumerate(self.shapes):
             nbytes = acc.weight_bytes(N, K)
             if nbytes not in bufs:
-                import numpy as np
                 bufs[nbytes] = np.empty(nbytes, dtype=np.uint8)
             host = bufs[nbytes]
             synth.weights(N, K, tensor=i + 1, seed=SEED, out=host.reshape(N, -1))
-            if arena:
-                d = self.arena[offs[i]:offs[i] + nbytes]
-            else:
-                d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            d = self.arena[offs[i]:offs[i] + nbytes]
             d.copy_(torch.from_numpy(host))
             self.W.append(d)
             if i % 64 == 0:
@@ -105,44 +134,56 @@ class Pass:
             % (len(self.shapes), self.weight_bytes / 1e9, time.time() - t0))
         self.x = {}
         self.y = {}
+        Ns = sorted({N for _, N, _ in self.shapes} | {5 * 5120})
         for M in ms:
             for K in sorted({K for _, _, K in self.shapes}):
                 xs = synth.acts(M, K, tensor=100000 + K, seed=SEED)
                 self.x[(M, K)] = torch.from_numpy(xs).to(dev)
-            for N in sorted({N for _, N, _ in self.shapes}):
+            for N in Ns:
                 self.y[(M, N)] = torch.empty((M, N), dtype=torch.float32, device=dev)
         self.lib = sbb.load()
         self.h = sbb.qmm_create(0)
         self.calls = {}
+        self.fused_calls = {}
+        vp = ctypes.c_void_p
         for M in ms:
-            lst = []
+            lst, fl = [], []
             for (name, N, K), Wd in zip(self.shapes, self.W):
-                lst.append((ctypes.c_void_p(self.x[(M, K)].data_ptr()), ctypes.c_void_p(Wd.data_ptr()),
-                            ctypes.c_void_p(self.y[(M, N)].data_ptr()), M, N, K))
+                c = (vp(self.x[(M, K)].data_ptr()), vp(Wd.data_ptr()), vp(self.y[(M, N)].data_ptr()), M, N, K)
+                lst.append(c)
+                if name.endswith(".proj0"):  # projections 0..4 as one 25600-row call
+                    fl.append((c[0], c[1], vp(self.y[(M, 5 * 5120)].data_ptr()), M, 5 * N, K))
+                elif ".proj" in name and not name.endswith(".proj5"):
+                    continue
+                else:
+                    fl.append(c)
             self.calls[M] = lst
+            self.fused_calls[M] = fl
         self.graphs = {}
+        self.fused_graphs = {}
 
-    def run(self, M, stream_ptr):
+    def run(self, M, stream_ptr, fused=False):
         fn, h = self.lib.qmm_run, self.h
         s = ctypes.c_void_p(stream_ptr)
-        for x, w, y, m, n, k in self.calls[M]:
+        for x, w, y, m, n, k in (self.fused_calls if fused else self.calls)[M]:
             rc = fn(h, x, w, y, m, n, k, s)
             if rc:
                 raise RuntimeError("qmm_run failed: %s" % self.sbb.qmm_status_string(rc))
 
-    def capture(self):
+    def capture(self, fused=False, ms=None):
         torch = self.torch
-        for M in self.ms:
+        graphs = self.fused_graphs if fused else self.graphs
+        for M in (self.ms if ms is None else ms):
             g = torch.cuda.CUDAGraph()
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
-                self.run(M, side.cuda_stream)  # warm the kernels outside the capture
+                self.run(M, side.cuda_stream, fused)  # warm the kernels outside the capture
             torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
             with torch.cuda.graph(g):
-                self.run(M, torch.cuda.current_stream().cuda_stream)
-            self.graphs[M] = g
+                self.run(M, torch.cuda.current_stream().cuda_stream, fused)
+            graphs[M] = g
         torch.cuda.synchronize()
 
     def plan(self, M, N, K):
@@ -155,12 +196,13 @@ class Pass:
         return "qmm_vector_kernel<%d>" % M
 
 
-def time_passes(P, steps, warmup, graph, ms=None):
+def time_passes(P, steps, warmup, graph, ms=None, fused=False):
     """Per-M ms per pass (for the row counts ms, default all of P's), timed with
     HIP events on the stream the kernels run on."""
     torch = P.torch
     stream = torch.cuda.current_stream()
     ms = P.ms if ms is None else ms
+    graphs = P.fused_graphs if fused else P.graphs
     ev = {M: [] for M in ms}
 
     def one_step(record):
@@ -169,9 +211,9 @@ def time_passes(P, steps, warmup, graph, ms=None):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
             if graph:
-                P.graphs[M].replay()
+                graphs[M].replay()
             else:
-                P.run(M, stream.cuda_stream)
+                P.run(M, stream.cuda_stream, fused)
             if record:
                 b.record(stream)
                 ev[M].append((a, b))
@@ -193,82 +235,276 @@ def time_passes(P, steps, warmup, graph, ms=None):
     return total_ms / steps, per_m, wall
 
 
-def kernel_timing(P, M_list):
-    """Every launch of one eager pass per M bracketed by HIP events on its stream:
-    per-symbol launch count, mean duration and algorithmic bytes per launch."""
+def kernel_timing(P, M_list, seq=None):
+    """One eager pass per M in which every launch records HIP events at the
+    start and end of its own kernel (qmm_set_launch_events): per-symbol and
+    per-(shape, M) launch counts, mean kernel durations and algorithmic bytes.
+    seq, if a list, receives the launch sequence (symbol, shape, M) in order."""
     from skinny_bit_block_amd import accounting as acc
-    torch = P.torch
+    from skinny_bit_block_amd.events import EventPool
+    torch, sbb = P.torch, P.sbb
     stream = torch.cuda.current_stream()
+    pool = EventPool(max(len(P.calls[M]) for M in M_list))
     recs = []
     for M in M_list:
-        for (name, N, K), call in zip(P.shapes, P.calls[M]):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            rc = P.lib.qmm_run(P.h, call[0], call[1], call[2], M, N, K, ctypes.c_void_p(stream.cuda_stream))
+        for i, call in enumerate(P.calls[M]):
+            x, w, y, m, N, K = call
+            sbb.qmm_set_launch_events(P.h, *pool.pairs[i])
+            rc = P.lib.qmm_run(P.h, x, w, y, M, N, K, ctypes.c_void_p(stream.cuda_stream))
             if rc:
-                raise RuntimeError(P.sbb.qmm_status_string(rc))
-            b.record(stream)
-            recs.append((P.kernel_symbol(M, N, K), M, N, K, a, b))
-    torch.cuda.synchronize()
-    sym = {}
-    for s, M, N, K, a, b in recs:
-        d = sym.setdefault(s, {"launches": 0, "ms": 0.0, "bytes": 0, "weight_bytes": 0})
-        d["launches"] += 1
-        d["ms"] += a.elapsed_time(b)
-        d["bytes"] += acc.call_bytes(M, N, K)
-        d["weight_bytes"] += acc.weight_bytes(N, K)
-        acc.check_roofline(acc.weight_bytes(N, K), a.elapsed_time(b) * 1e-3, what="%s M=%d N=%d K=%d" % (s, M, N, K))
-    return sym
+                raise RuntimeError(sbb.qmm_status_string(rc))
+        torch.cuda.synchronize()
+        for i, (x, w, y, m, N, K) in enumerate(P.calls[M]):
+            recs.append((P.kernel_symbol(M, N, K), shape_class(N, K), M, N, K, pool.elapsed_ms(i)))
+    pool.close()
+    sym, shp = {}, {}
+    for s, cls, M, N, K, ms_ in recs:
+        us = ms_ * 1e3
+        acc.check_roofline(acc.weight_bytes(N, K), us * 1e-6, what="%s M=%d N=%d K=%d" % (s, M, N, K))
+        for key, table in ((s, sym), ("%s M=%d" % (cls, M), shp)):
+            d = table.setdefault(key, {"launches": 0, "us": 0.0, "bytes": 0, "weight_bytes": 0})
+            d["launches"] += 1
+            d["us"] += us
+            d["bytes"] += acc.call_bytes(M, N, K)
+            d["weight_bytes"] += acc.weight_bytes(N, K)
+        if seq is not None:
+            seq.append({"symbol": s, "shape": cls, "M": M, "N": N, "K": K})
+    return sym, shp
 
 
-def read_traffic(symbol):
-    """Counter-measured HBM bytes per dispatch of `symbol`, from the committed
-    rocprofv3 summary, or None if absent or taken on other kernel source."""
-    path = os.path.join(ROOT, "profiles", "counters_full_pass.txt")
+def read_profile(name):
+    """key -> value lines of a committed profile summary under profiles/, or {}
+    when it is absent or was taken on other kernel source."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
-        return None
-    sha, val = None, None
+        return {}
+    vals, sha = {}, None
     for line in open(path):
         if line.startswith("kernel_source_sha256:"):
             sha = line.split(":", 1)[1].strip()
-        if line.startswith("traffic_bytes_per_dispatch[%s]:" % symbol):
-            val = float(line.split(":", 1)[1].strip())
-    if sha != kernel_source_sha() or val is None:
-        return None
-    return val
+        elif line.startswith("traffic_bytes_per_dispatch[") and "]:" in line:
+            key = line[len("traffic_bytes_per_dispatch["):line.index("]:")]
+            vals[key] = float(line.split("]:", 1)[1].strip())
+    return vals if sha == kernel_source_sha() else {}
 
 
-def cpu_baseline(budget_s):
-    """The oracle as it stands on the host cores: rows of one gate+up matrix
-    (N = 34816, K = 5120) at M = 1, 4, 8, 16, cycling over the matrix in
-    chunks until each M has used a quarter of the time budget."""
+def configs_measure(torch, sbb, synth, acc, h, ceiling_gbs=None, reps=4):
+    """The single-matrix workloads, each walking distinct device copies so that
+    at least 1 GiB streams between two reads of the same bytes (the 256 MB
+    last-level cache cannot serve them): per row count, us per call of a
+    graph-replayed sequence (launch gaps included), the kernel's own duration
+    (event-timed eager launches over the same copies), weight GB/s and % of
+    peak for both, and the HBM traffic per call from the committed counter
+    profile (profiles/counters_pass_and_configs.txt) with its GB/s."""
+    from skinny_bit_block_amd.events import EventPool
+    lib = sbb.load()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    traffic = read_profile("counters_pass_and_configs.txt")
+    rows = []
+    for name, N, K, Ms, xs in CONFIGS:
+        wb = acc.weight_bytes(N, K)
+        R = max(3, -(-(1 << 30) // wb))
+        base = torch.from_numpy(synth.weights(N, K, tensor=7, seed=SEED).reshape(-1)).cuda()
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        pool = EventPool(R)
+        for M in Ms:
+            x = torch.from_numpy(synth.acts(M, K, tensor=8, seed=SEED, scale=xs)).cuda()
+            y = torch.empty((M, N), device="cuda")
+            calls = [(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(c.data_ptr()),
+                      ctypes.c_void_p(y.data_ptr())) for c in copies]
+
+            def go(spp):
+                for c in calls:
+                    rc = lib.qmm_run(h, *c, M, N, K, ctypes.c_void_p(spp))
+                    if rc:
+                        raise RuntimeError(sbb.qmm_status_string(rc))
+
+            go(stream.cuda_stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                go(torch.cuda.current_stream().cuda_stream)
+            g.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e-3 / R)
+            ts.sort()
+            t = ts[len(ts) // 2]
+            # the kernel's own duration, eager launches walking the same copies
+            for i, c in enumerate(calls):
+                sbb.qmm_set_launch_events(h, *pool.pairs[i])
+                rc = lib.qmm_run(h, *c, M, N, K, sp)
+                if rc:
+                    raise RuntimeError(sbb.qmm_status_string(rc))
+            torch.cuda.synchronize()
+            kd = sorted(pool.elapsed_ms(i) * 1e-3 for i in range(len(calls)))[len(calls) // 2]
+            acc.check_roofline(wb, min(ts), what="%s M=%d" % (name, M))
+            acc.check_roofline(wb, kd, what="%s M=%d (kernel)" % (name, M))
+            p = sbb.qmm_query_plan(h, M, N, K)
+            key = "config %s M=%d" % (shape_class(N, K), M)
+            row = {"workload": name, "M": M, "us_per_call": round(t * 1e6, 3),
+                   "weight_gbs": round(acc.gbs(wb, t), 1), "pct_hbm_peak": round(acc.pct_of(wb, t, 8e12), 2),
+                   "kernel_us": round(kd * 1e6, 3), "kernel_weight_gbs": round(acc.gbs(wb, kd), 1),
+                   "kernel_pct_hbm_peak": round(acc.pct_of(wb, kd, 8e12), 2),
+                   "kernel": sbb.KERNEL_NAMES[p["kernel"]], "waves_per_wg": p["waves_per_wg"],
+                   "splits": p["splits"], "wave_splits": p["wave_splits"], "copies": R}
+            if ceiling_gbs:
+                row["pct_of_read_ceiling"] = round(100 * acc.gbs(wb, t) / ceiling_gbs, 2)
+            if key in traffic:
+                row["counter_bytes_per_call"] = int(traffic[key])
+                row["counter_gbs"] = round(traffic[key] / kd / 1e9, 1)
+                row["counter_pct_hbm_peak"] = round(100 * traffic[key] / kd / 8e12, 2)
+            rows.append(row)
+            log(json.dumps(row))
+        pool.close()
+        del copies, base
+        torch.cuda.empty_cache()
+    return rows
+
+
+def probes_measure(torch, acc):
+    """The memory system and launch path on their own (include/qmm_probe.h):
+    a read-only 128-bit streaming kernel over 4 GiB (best of a few grid
+    shapes), the same kernel reading one lm_head-sized buffer back to back for
+    ~100 ms (sustained read), and 513 empty kernels in a graph (the launch gap
+    between back-to-back launches of a pass)."""
+    from skinny_bit_block_amd import probe
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    best = None
+    for grid, block in ((512, 256), (2048, 256), (4096, 512)):
+        probe.qmm_probe_read(big.data_ptr(), big.numel(), grid, block, sink.data_ptr(), sp)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            probe.qmm_probe_read(big.data_ptr(), big.numel(), grid, block, sink.data_ptr(), sp)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        ts.sort()
+        gbs = acc.gbs(big.numel(), ts[2])
+        if best is None or gbs > best[0]:
+            best = (gbs, grid, block)
+    out["read_ceiling"] = {"bytes": big.numel(), "gbs": round(best[0], 1),
+                           "pct_hbm_peak": round(100 * best[0] / PEAK_GBS, 2),
+                           "grid": best[1], "block": best[2]}
+    del big
+    nb = acc.weight_bytes(151936, 5120)
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    buf.fill_(2)
+    reps = 200
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            probe.qmm_probe_read(buf.data_ptr(), nb, 2048, 256, sink.data_ptr(),
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3
+    out["sustained_read"] = {"bytes_per_read": nb, "reads": reps, "ms": round(t * 1e3, 2),
+                             "gbs": round(acc.gbs(nb * reps, t), 1),
+                             "pct_hbm_peak": round(acc.pct_of(nb * reps, t, 8e12), 2)}
+    del buf, g
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(513):
+            probe.qmm_probe_empty(256, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / 513)
+    ts.sort()
+    out["launch_gap_us"] = round(ts[2], 3)
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(budget_s, seconds_single=2.0):
+    """The oracle as it stands on the host cores. For each matrix shape of the
+    pass and each row count of the headline (1, 4, 8, 16), the oracle computes
+    rows of one seeded matrix of that shape in chunks for an equal share of
+    the budget; its weight GB/s per (shape, M) then gives the time of a whole
+    pass (the 513 calls' bytes at those rates), reported as the pass's weight
+    GB/s over the four row counts. The single 2048x2048 workload at M = 4 is
+    also timed whole on all threads and on one thread."""
     import numpy as np
     import oracle
     import synth
     from skinny_bit_block_amd import accounting as acc
-    N, K = 34816, 5120
-    W = synth.weights(N, K, tensor=1 + 6, seed=SEED)
-    per_m = budget_s / 4
-    chunk = 4096
-    total_bytes, total_s, rows_used = 0, 0.0, {}
-    for M in (1, 4, 8, 16):
-        x = synth.acts(M, K, tensor=100000 + K, seed=SEED)
-        rows, t0, start = 0, time.time(), 0
-        while time.time() - t0 < per_m:
-            idx = np.arange(start, min(N, start + chunk))
-            oracle.qmm_rows(x, W, N, K, idx)
-            rows += idx.size
-            start = 0 if start + chunk >= N else start + chunk
-        dt = time.time() - t0
-        total_bytes += acc.weight_bytes(rows, K)
-        total_s += dt
-        rows_used[M] = rows
-    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": "fp64 oracle on rows of one gate+up matrix (N=34816, K=5120), cycled in chunks "
-                      "of 4096 rows: %s rows at M=1/4/8/16, %.1f s of wall time on %d threads; "
-                      "weight GB/s over the sample"
-                      % ("/".join(str(rows_used[m]) for m in (1, 4, 8, 16)), total_s, oracle.threads())}
+    shapes = [("square", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408),
+              ("lm_head", 151936, 5120)]
+    Ms = (1, 4, 8, 16)
+    share = budget_s / (len(shapes) * len(Ms))
+    rates, rows_used = {}, {}
+    total_s = 0.0
+    for cls, N, K in shapes:
+        W = synth.weights(min(N, 8192), K, tensor=1 + 6, seed=SEED)  # rows of one matrix
+        n_avail = W.shape[0]
+        chunk = 1024 if K <= 5120 else 256
+        for M in Ms:
+            x = synth.acts(M, K, tensor=100000 + K, seed=SEED)
+            rows, t0, start = 0, time.time(), 0
+            while time.time() - t0 < share:
+                idx = np.arange(start, min(n_avail, start + chunk))
+                oracle.qmm_rows(x, W, n_avail, K, idx)
+                rows += idx.size
+                start = 0 if start + chunk >= n_avail else start + chunk
+            dt = time.time() - t0
+            total_s += dt
+            rates[(cls, M)] = acc.weight_bytes(rows, K) / dt
+            rows_used["%s M=%d" % (cls, M)] = rows
+    pass_s = {M: sum(acc.weight_bytes(N, K) / rates[(shape_class(N, K), M)]
+                     for _, N, K in acc.full_pass_shapes()) for M in Ms}
+    pass_bytes = acc.full_pass_weight_bytes()
+    value = pass_bytes * len(Ms) / sum(pass_s.values()) / 1e9
+    # the single projection, whole, all threads and one thread
+    N, K, M = 2048, 2048, 4
+    W = synth.weights(N, K, tensor=7, seed=SEED)
+    x = synth.acts(M, K, tensor=8, seed=SEED)
+    single = {}
+    for threads in (0, 1):
+        n, t0 = 0, time.time()
+        while time.time() - t0 < seconds_single:
+            oracle.qmm(x, W, N, K, nthreads=threads)
+            n += 1
+        dt = (time.time() - t0) / n
+        total_s += dt * n
+        single["all_threads" if threads == 0 else "one_thread"] = {
+            "ms_per_call": round(dt * 1e3, 3), "weight_gbs": round(acc.gbs(acc.weight_bytes(N, K), dt), 4)}
+    return {"value": round(value, 4), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "fp64 oracle on rows of one seeded matrix of each pass shape (5120x5120, "
+                      "34816x5120, 5120x17408, 151936x5120; up to 8192 rows) at M=1/4/8/16, "
+                      "%.1f s of wall time on %d threads; value = weight GB/s of a whole pass "
+                      "(513 calls' bytes at the sampled per-shape rates) over the four row counts"
+                      % (total_s, oracle.threads()),
+            "ms_per_pass": {str(M): round(pass_s[M] * 1e3, 1) for M in Ms},
+            "per_shape_gbs": {"%s M=%d" % k: round(v / 1e9, 4) for k, v in sorted(rates.items())},
+            "single_2048x2048_m4": single}
 
 
 def ids_measure(torch, sbb, synth, acc, h, reps=5):
@@ -445,51 +681,91 @@ def int4_measure(torch, sbb, synth, acc, h, reps=5):
                         "seeded random codes, 144-byte groups", "shapes": out}
 
 
+def pass_record(P, per_m, acc, ceiling=None):
+    out = {}
+    for M, ms_ in per_m.items():
+        r = {"ms_per_pass": round(ms_, 4),
+             "weight_gbs": round(acc.gbs(P.weight_bytes, ms_ * 1e-3), 1),
+             "pct_hbm_peak": round(acc.pct_of(P.weight_bytes, ms_ * 1e-3, 8e12), 2)}
+        if ceiling:
+            r["pct_of_read_ceiling"] = round(100 * acc.gbs(P.weight_bytes, ms_ * 1e-3) / ceiling, 2)
+        out[str(M)] = r
+    return out
+
+
 def mode_pass(args, torch, sbb, synth, acc):
     ms = [int(v) for v in args.ms.split(",")]
     extra = [int(v) for v in args.extra_ms.split(",") if v and int(v) not in ms]
-    P = Pass(torch, sbb, synth, acc, ms + extra, args.layers, arena=not args.separate)
+    P = Pass(torch, sbb, synth, acc, ms + extra, args.layers)
     if not args.no_graph:
         P.capture()
+        if not args.no_fused:
+            P.capture(fused=True)
         log("graphs captured")
     ms_step, per_m, wall = time_passes(P, args.steps, args.warmup, graph=not args.no_graph, ms=ms)
     log("timed %d steps: %.3f ms/step (wall %.2f s)" % (args.steps, ms_step, wall))
     for M in ms:
         acc.check_roofline(P.weight_bytes, per_m[M] * 1e-3, what="pass M=%d" % M)
     out = {}
-    out["per_m"] = {str(M): {"ms_per_pass": round(per_m[M], 4),
-                             "weight_gbs": round(acc.gbs(P.weight_bytes, per_m[M] * 1e-3), 1),
-                             "pct_hbm_peak": round(acc.pct_of(P.weight_bytes, per_m[M] * 1e-3, 8e12), 2)}
-                    for M in ms}
+    probes = None
+    if not args.no_probes:
+        log("memory-system probes...")
+        probes = probes_measure(torch, acc)
+    ceiling = probes["read_ceiling"]["gbs"] if probes else None
+    out["per_m"] = pass_record(P, per_m, acc, ceiling)
+    x_per_m = {}
     if extra:
         _, x_per_m, _ = time_passes(P, args.steps, args.warmup, graph=not args.no_graph, ms=extra)
         for M in extra:
             acc.check_roofline(P.weight_bytes, x_per_m[M] * 1e-3, what="pass M=%d" % M)
-        out["per_m_extra"] = {str(M): {"ms_per_pass": round(x_per_m[M], 4),
-                                       "weight_gbs": round(acc.gbs(P.weight_bytes, x_per_m[M] * 1e-3), 1),
-                                       "pct_hbm_peak": round(acc.pct_of(P.weight_bytes, x_per_m[M] * 1e-3, 8e12), 2)}
-                              for M in extra}
+        out["per_m_extra"] = pass_record(P, x_per_m, acc, ceiling)
+    if not args.no_fused and not args.no_graph:
+        log("fused-projection pass...")
+        f_step, f_per_m, _ = time_passes(P, args.steps, args.warmup, graph=True, ms=ms + extra,
+                                         fused=True)
+        for M in ms + extra:
+            acc.check_roofline(P.weight_bytes, f_per_m[M] * 1e-3, what="fused pass M=%d" % M)
+        fm = ms
+        out["fused_pass"] = {
+            "workload": "the same 15.73 GB with each layer's five same-input 5120-wide projections "
+                        "as one 25600x5120 call (the sixth, gate+up and down separate): %d calls"
+                        % len(P.fused_calls[ms[0]]),
+            "weight_gbs": round(acc.gbs(P.weight_bytes * len(fm), sum(f_per_m[M] for M in fm) * 1e-3), 1),
+            "per_m": pass_record(P, f_per_m, acc, ceiling)}
     if not args.no_eager and not args.no_graph:
         e_step, e_per_m, _ = time_passes(P, max(3, args.steps // 4), 1, graph=False, ms=ms)
         out["eager"] = {str(M): {"ms_per_pass": round(e_per_m[M], 4),
                                  "weight_gbs": round(acc.gbs(P.weight_bytes, e_per_m[M] * 1e-3), 1)}
                         for M in ms}
-    sym = kernel_timing(P, ms)
-    dom = max(sym, key=lambda s: sym[s]["ms"])
+    sym, shp = kernel_timing(P, ms)
+    dom = max(sym, key=lambda k: sym[k]["us"])
     d = sym[dom]
-    avg_s = d["ms"] / d["launches"] * 1e-3
+    avg_s = d["us"] / d["launches"] * 1e-6
     bytes_per_launch = d["bytes"] / d["launches"]
     achieved = bytes_per_launch / avg_s / 1e9
-    traffic = read_traffic(dom)
+    traffic = read_profile("counters_pass_and_configs.txt").get(dom)
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                        "frac": round(achieved / PEAK_GBS, 4),
                        "traffic": None if traffic is None else round(traffic, 0),
                        "kernel": dom, "launches": d["launches"],
-                       "avg_launch_us": round(avg_s * 1e6, 3),
-                       "algorithmic_bytes_per_launch": round(bytes_per_launch, 0)}
-    out["kernels"] = {s: {"launches": v["launches"], "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
-                          "share": round(v["ms"] / sum(w["ms"] for w in sym.values()), 4)}
-                      for s, v in sorted(sym.items())}
+                       "avg_kernel_us": round(avg_s * 1e6, 3),
+                       "algorithmic_bytes_per_launch": round(bytes_per_launch, 0),
+                       "timing": "kernel start to end (HIP events recorded by the launch itself), "
+                                 "one eager pass per M in %s" % ms}
+    if ceiling:
+        out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
+    out["kernels"] = {k: {"launches": v["launches"], "avg_us": round(v["us"] / v["launches"], 3),
+                          "share": round(v["us"] / sum(w["us"] for w in sym.values()), 4)}
+                      for k, v in sorted(sym.items())}
+    out["kernel_per_shape"] = {k: {"launches": v["launches"], "avg_us": round(v["us"] / v["launches"], 3),
+                                   "weight_gbs": round(v["weight_bytes"] / (v["us"] * 1e-6) / 1e9, 1),
+                                   "pct_hbm_peak": round(100 * v["weight_bytes"] / (v["us"] * 1e-6) / 8e12, 2)}
+                               for k, v in sorted(shp.items())}
+    if probes:
+        out["probes"] = probes
+    if not args.no_configs:
+        log("single-matrix workloads...")
+        out["configs"] = configs_measure(torch, sbb, synth, acc, P.h, ceiling)
     if not args.no_ids:
         log("expert-indexed product...")
         out["ids"] = ids_measure(torch, sbb, synth, acc, P.h)
@@ -500,6 +776,7 @@ def mode_pass(args, torch, sbb, synth, acc):
         log("plain INT4 product...")
         out["int4"] = int4_measure(torch, sbb, synth, acc, P.h)
     value = acc.gbs(P.weight_bytes * len(ms), ms_step * 1e-3)
+    prop = torch.cuda.get_device_properties(0)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -511,8 +788,12 @@ def mode_pass(args, torch, sbb, synth, acc):
                    "rows_per_pass": ms, "passes_per_step": len(ms),
                    "timing": "hipGraph replay" if not args.no_graph else "eager",
                    "pct_hbm_peak": round(100 * value / PEAK_GBS, 2),
-                   "floor_ms_per_pass": round(P.weight_bytes / 8e12 * 1e3, 4)},
+                   "floor_ms_per_pass": round(P.weight_bytes / 8e12 * 1e3, 4),
+                   "device": "%s, %d CUs" % (getattr(prop, "gcnArchName", prop.name),
+                                            prop.multi_processor_count)},
     }
+    if ceiling:
+        line["config"]["pct_of_read_ceiling"] = round(100 * value / ceiling, 2)
     line.update(out)
     line["kernel_source_sha256"] = kernel_source_sha()
     if not args.no_cpu:
@@ -523,63 +804,45 @@ def mode_pass(args, torch, sbb, synth, acc):
 
 
 def mode_kernels(args, torch, sbb, synth, acc):
-    """Only the per-launch timing region (one eager pass per M): for rocprofv3."""
+    """Only event-timed eager launches, for rocprofv3 runs: one pass per M,
+    then two calls of each single-matrix workload per row count (on two
+    distinct copies). --seq-out writes the launch sequence (symbol, shape, M)
+    that profile_summary.py maps the profiler's dispatches onto."""
     ms = [int(v) for v in args.ms.split(",")]
-    P = Pass(torch, sbb, synth, acc, ms, args.layers, arena=not args.separate)
+    P = Pass(torch, sbb, synth, acc, ms, args.layers)
+    from skinny_bit_block_amd.events import EventPool
+    seq = []
     for _ in range(max(1, args.steps)):
-        sym = kernel_timing(P, ms)
-    print(json.dumps({s: {"launches": v["launches"], "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
-                          "bytes_per_launch": v["bytes"] / v["launches"]} for s, v in sorted(sym.items())}))
-
-
-def mode_configs(args, torch, sbb, synth, acc):
-    """The single-matrix workloads, rotating distinct copies so that >= 1 GiB is
-    streamed between two reads of the same bytes (the 256 MB last-level cache
-    cannot serve them)."""
-    cfgs = [("single 2048x2048", 2048, 2048, [4], 1.0),
-            ("gate+up 34816x5120", 34816, 5120, [1, 2, 4, 7, 8, 9, 16], 1.0),
-            ("down 5120x17408", 5120, 17408, [1, 4, 8, 16], 0.1),
-            ("lm_head 151936x5120", 151936, 5120, [1, 7], 1.0)]
-    h = sbb.qmm_create(0)
+        sym, shp = kernel_timing(P, ms, seq)
+    pool = EventPool(1)
     lib = sbb.load()
     stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    rows = []
-    for name, N, K, Ms, xs in cfgs:
-        wb = acc.weight_bytes(N, K)
-        R = max(3, -(-(1 << 30) // wb))
-        base = torch.from_numpy(synth.weights(N, K, tensor=7, seed=SEED).reshape(-1)).cuda()
-        copies = [base] + [base.clone() for _ in range(R - 1)]
+    for name, N, K, Ms, xs in CONFIGS:
+        Ws = [torch.from_numpy(synth.weights(N, K, tensor=7 + i, seed=SEED).reshape(-1)).cuda()
+              for i in range(2)]
         for M in Ms:
             x = torch.from_numpy(synth.acts(M, K, tensor=8, seed=SEED, scale=xs)).cuda()
             y = torch.empty((M, N), device="cuda")
-            calls = [(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(c.data_ptr()),
-                      ctypes.c_void_p(y.data_ptr())) for c in copies]
-            n_launch = max(R * 4, int(0.05 / max(wb / 8e12, 1e-7)))
-            for i in range(R * 2):
-                lib.qmm_run(h, *calls[i % R], M, N, K, sp)
-            torch.cuda.synchronize()
-            meds = []
-            for _ in range(5):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for i in range(n_launch):
-                    lib.qmm_run(h, *calls[i % R], M, N, K, sp)
-                b.record(stream)
-                torch.cuda.synchronize()
-                meds.append(a.elapsed_time(b) / n_launch)
-            meds.sort()
-            t = meds[2] * 1e-3
-            acc.check_roofline(wb, meds[0] * 1e-3, what="%s M=%d" % (name, M))
-            p = sbb.qmm_query_plan(h, M, N, K)
-            rows.append({"workload": name, "M": M, "us_per_call": round(t * 1e6, 3),
-                         "weight_gbs": round(acc.gbs(wb, t), 1),
-                         "pct_hbm_peak": round(acc.pct_of(wb, t, 8e12), 2),
-                         "kernel": sbb.KERNEL_NAMES[p["kernel"]], "splits": p["splits"],
-                         "waves_per_wg": p["waves_per_wg"], "copies": R})
-            log(json.dumps(rows[-1]))
-        del copies, base
-        torch.cuda.empty_cache()
+            for W in Ws:
+                sbb.qmm_set_launch_events(P.h, *pool.pairs[0])
+                rc = lib.qmm_run(P.h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(W.data_ptr()),
+                                 ctypes.c_void_p(y.data_ptr()), M, N, K, ctypes.c_void_p(stream.cuda_stream))
+                if rc:
+                    raise RuntimeError(sbb.qmm_status_string(rc))
+                seq.append({"symbol": P.kernel_symbol(M, N, K), "shape": "config " + shape_class(N, K),
+                            "M": M, "N": N, "K": K})
+        torch.cuda.synchronize()
+        del Ws
+    if args.seq_out:
+        json.dump({"kernel_source_sha256": kernel_source_sha(), "launches": seq}, open(args.seq_out, "w"))
+    print(json.dumps({k: {"launches": v["launches"], "avg_us": round(v["us"] / v["launches"], 3)}
+                      for k, v in sorted(sym.items())}))
+
+
+def mode_configs(args, torch, sbb, synth, acc):
+    """The single-matrix workloads only."""
+    h = sbb.qmm_create(0)
+    rows = configs_measure(torch, sbb, synth, acc, h)
     sbb.qmm_destroy(h)
     print(json.dumps({"configs": rows}))
 

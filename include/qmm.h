@@ -221,7 +221,8 @@ uint64_t qmm_weight_bytes(int64_t N, int64_t K);
 /* Kernels of the launch table. */
 enum {
   QMM_KERNEL_AUTO = 0,  /* let the launch table decide (for overrides) */
-  QMM_KERNEL_VECTOR = 1, /* row-vector kernel: VALU dot products, x broadcast */
+  QMM_KERNEL_VECTOR = 1, /* row-vector kernel: VALU dot products, x broadcast;
+                            1..8 rows (its work grows with every row) */
   QMM_KERNEL_TILED = 2   /* tiled kernel: MFMA 16x16x32 f16 (rows padded to 16) */
 };
 
@@ -251,7 +252,8 @@ typedef struct {
 int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out);
 
 /* Force a kernel for every following call on this handle (QMM_KERNEL_AUTO
- * restores the table). For tests and sweeps. */
+ * restores the table). For tests and sweeps. A call that forces the
+ * row-vector kernel above 8 rows returns QMM_ERR_INVALID_ARG. */
 int qmm_set_kernel(qmm_handle h, int kernel);
 
 /* Override the grid shape for every following call: waves_per_wg (0 = table,
@@ -267,6 +269,15 @@ int qmm_set_shape(qmm_handle h, int waves_per_wg, int splits, int grid_x);
  * call (0 = table, else 1..8; waves_per_wg must be a multiple and splits at
  * least this, or qmm_run returns QMM_ERR_INVALID_ARG). For sweeps. */
 int qmm_set_wave_splits(qmm_handle h, int wave_splits);
+
+/* For measurement: the next launch made through this handle (any qmm_run*
+ * call) records `start` when its kernel begins executing and `stop` when it
+ * ends (hipExtLaunchKernel), so that hipEventElapsedTime(start, stop) is the
+ * kernel's own duration without the launch overhead around it; the events
+ * are then forgotten (one launch only). Events are created by the caller on
+ * the handle's device; NULL, NULL clears them. Not for use under graph
+ * capture. Returns QMM_ERR_INVALID_ARG for a null handle. */
+int qmm_set_launch_events(qmm_handle h, hipEvent_t start, hipEvent_t stop);
 
 /* The row count from which the launch table switches from the row-vector to
  * the tiled kernel (M >= switch uses the tiled kernel). */

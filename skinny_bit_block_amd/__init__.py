@@ -32,7 +32,7 @@ KERNEL_NAMES = {KERNEL_VECTOR: "vector", KERNEL_TILED: "tiled"}
 EXPORTS = ["qmm_create", "qmm_run", "qmm_run_static", "qmm_run_ids", "qmm_run_nvfp4", "qmm_nvfp4_repack",
            "qmm_run_int4", "qmm_int4_repack", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
            "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_wave_splits",
-           "qmm_switch_point"]
+           "qmm_switch_point", "qmm_set_launch_events"]
 
 
 class qmm_plan(ctypes.Structure):
@@ -89,6 +89,8 @@ def load():
         lib.qmm_set_wave_splits.restype = ctypes.c_int
         lib.qmm_switch_point.argtypes = [vp, i64, i64]
         lib.qmm_switch_point.restype = ctypes.c_int
+        lib.qmm_set_launch_events.argtypes = [vp, vp, vp]
+        lib.qmm_set_launch_events.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -308,6 +310,16 @@ def qmm_set_kernel(h, kernel):
 
 def qmm_set_shape(h, waves_per_wg=0, splits=0, grid_x=0):
     return _check(load().qmm_set_shape(h, int(waves_per_wg), int(splits), int(grid_x)))
+
+
+def qmm_set_launch_events(h, start=None, stop=None):
+    """Events (torch.cuda.Event or raw hipEvent_t) recorded around the kernel of
+    the next launch on this handle: its own duration, without launch overhead."""
+    def ev(e):
+        if e is None:
+            return None
+        return e if isinstance(e, int) else e.cuda_event
+    return _check(load().qmm_set_launch_events(h, ev(start), ev(stop)))
 
 
 def qmm_set_wave_splits(h, wave_splits=0):

@@ -36,6 +36,7 @@ struct qmm_ctx {
   unsigned* counters;   // split-K arrival counters, one per row tile, zeroed at creation
   int64_t max_counter_tiles;  // row tiles the counters cover
   bool fixed_scratch;   // the static scratch: a plan that does not fit is QMM_ERR_SCRATCH
+  hipEvent_t ev_start, ev_stop;  // events for the next launch only (measurement)
 };
 
 namespace {
@@ -174,6 +175,7 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
     kernel = QMM_KERNEL_TILED;
     te = nullptr;  // table entries are for plain calls
   }
+  if (kernel == QMM_KERNEL_VECTOR && M > qmm::kMaxVectorRows) return QMM_ERR_INVALID_ARG;
   if (groups_fmt) {
     if (h->forced_kernel == QMM_KERNEL_VECTOR) return QMM_ERR_INVALID_ARG;
     kernel = QMM_KERNEL_TILED;  // launch shape from the table: the same group geometry
@@ -253,6 +255,13 @@ int make_plan(qmm_ctx* h, int64_t M, int64_t N, int64_t K, qmm_plan* p, int slot
   return QMM_OK;
 }
 
+// Measurement events set with qmm_set_launch_events go to the next launch only.
+void take_events(qmm_ctx* h, qmm::Launch& a) {
+  a.ev_start = h->ev_start;
+  a.ev_stop = h->ev_stop;
+  h->ev_start = h->ev_stop = nullptr;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
   return pa < pb + nb && pb < pa + na;
@@ -295,6 +304,7 @@ int qmm_create(qmm_handle* out, int device) {
   h->counters = nullptr;
   h->max_counter_tiles = qmm::kMaxCounterTiles;
   h->fixed_scratch = false;
+  h->ev_start = h->ev_stop = nullptr;
   h->nocc = 0;
   if (device == -1) {  // planning-only handle
     *out = h;
@@ -384,6 +394,13 @@ int qmm_set_wave_splits(qmm_handle h, int wave_splits) {
   return QMM_OK;
 }
 
+int qmm_set_launch_events(qmm_handle h, hipEvent_t start, hipEvent_t stop) {
+  if (!h) return QMM_ERR_INVALID_ARG;
+  h->ev_start = start;
+  h->ev_stop = stop;
+  return QMM_OK;
+}
+
 int qmm_switch_point(qmm_handle h, int64_t N, int64_t K) {
   if (!h) return QMM_ERR_INVALID_ARG;
   return table_switch(N, K);
@@ -428,6 +445,7 @@ int qmm_run(qmm_handle h, const float* x, const void* W_blocks, float* y, int64_
   a.expert_bytes = 0;
   a.slots = 1;
   a.oscale = 1.0f;
+  take_events(h, a);
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 
@@ -474,6 +492,7 @@ int qmm_run_ids(qmm_handle h, const float* x, const void* W_experts, const int32
   a.expert_bytes = (long long)expert_bytes;
   a.slots = slots;
   a.oscale = 1.0f;
+  take_events(h, a);
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 
@@ -542,6 +561,7 @@ int qmm_run_nvfp4(qmm_handle h, const float* x, const void* W_groups, float tens
   a.expert_bytes = 0;
   a.slots = 1;
   a.oscale = tensor_scale;
+  take_events(h, a);
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 
@@ -615,6 +635,7 @@ int qmm_run_int4(qmm_handle h, const float* x, const void* W_groups, float* y, i
   a.expert_bytes = 0;
   a.slots = 1;
   a.oscale = 1.0f;
+  take_events(h, a);
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 
@@ -698,6 +719,7 @@ int qmm_run_static(const float* x, const void* W_blocks, float* y, int64_t M, in
   a.expert_bytes = 0;
   a.slots = 1;
   a.oscale = 1.0f;
+  take_events(h, a);
   return qmm::launch(a, stream) == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 

@@ -13,6 +13,9 @@ constexpr int kBlockBytes = 144;    // bytes per super-block
 // where a unit goes (see the kernel file).
 constexpr int kLdsMax = 160 * 1024;  // LDS a workgroup may allocate on gfx950
 constexpr int kMaxWavesPerWg = 8;
+// The row-vector kernel's VALU work grows with every row while the tiled
+// kernel's does not; it is built for up to this many rows.
+constexpr int kMaxVectorRows = 8;
 
 struct Launch {
   int kernel;       // 1 = row-vector, 2 = tiled (MFMA), 3 = tiled, expert-indexed,
@@ -38,6 +41,9 @@ struct Launch {
   long long expert_bytes;
   int slots;
   float oscale;     // FP4 calls: the tensor scale, applied to every output (1 otherwise)
+  // measurement: when set, the launch records these events at the start and
+  // the end of the kernel itself (hipExtLaunchKernel)
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
 };
 
 // Row tiles a split-K call may have (one arrival counter each).

@@ -56,6 +56,7 @@
 // stage still outstanding), converts, and stores in the kernel's LDS layout;
 // the tiled layout XORs each unit's row slot with a function of its position
 // so the stores spread over all LDS banks (x_lead, x_issue, x_finish below).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1212,13 +1213,12 @@ __global__ void __launch_bounds__(512) qmm_tiled_kernel(const float* __restrict_
   }
 }
 
-// Entry points: [rows - 1] for the row-vector kernel, [MFMA row tiles - 1]
-// for the tiled kernel.
+// Entry points: [rows - 1] for the row-vector kernel (1..8 rows: its VALU
+// work grows with every row, and the tiled kernel is faster from 2 rows),
+// [MFMA row tiles - 1] for the tiled kernel.
 #define QMM_V(m) reinterpret_cast<const void*>(&qmm_vector_kernel<m>)
-#define QMM_V8(b) QMM_V(b + 1), QMM_V(b + 2), QMM_V(b + 3), QMM_V(b + 4), \
-                  QMM_V(b + 5), QMM_V(b + 6), QMM_V(b + 7), QMM_V(b + 8)
-const void* const kVectorFn[32] = {QMM_V8(0), QMM_V8(8), QMM_V8(16), QMM_V8(24)};
-#undef QMM_V8
+const void* const kVectorFn[kMaxVectorRows] = {QMM_V(1), QMM_V(2), QMM_V(3), QMM_V(4),
+                                               QMM_V(5), QMM_V(6), QMM_V(7), QMM_V(8)};
 #undef QMM_V
 // [plain, expert-indexed, block-scaled FP4, plain INT4][row tiles - 1]
 const void* const kTiledFn[4][2] = {
@@ -1233,7 +1233,7 @@ const void* const kTiledFn[4][2] = {
 
 const void* kernel_fn(int kernel, int M) {
   if (M < 1 || M > 32) return nullptr;
-  if (kernel == 1) return kVectorFn[M - 1];
+  if (kernel == 1) return M <= kMaxVectorRows ? kVectorFn[M - 1] : nullptr;
   if (kernel >= 2 && kernel <= 5) return kTiledFn[kernel - 2][M > 16 ? 1 : 0];
   return nullptr;
 }
@@ -1278,7 +1278,7 @@ hipError_t clear_counters(unsigned* counters, int n, hipStream_t stream) {
 }
 
 hipError_t prepare_kernels() {
-  for (int m = 0; m < 32; ++m) {
+  for (int m = 0; m < kMaxVectorRows; ++m) {
     hipError_t e = hipFuncSetAttribute(kVectorFn[m], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
   }
@@ -1313,9 +1313,15 @@ hipError_t launch(const Launch& a, hipStream_t stream) {
   if (a.kernel != 1) {
     void* args[] = {&x, &W, &y, &ws, &counters, &M, &N, &K, &nbs, &wsplit, &xs_m, &ss_m,
                     &ids, &E, &expert_bytes, &oscale};
+    if (a.ev_start || a.ev_stop)
+      return hipExtLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream, a.ev_start,
+                                a.ev_stop, 0);
     return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
   }
   void* args[] = {&x, &W, &y, &ws, &counters, &N, &K, &nbs, &wsplit, &xs_m, &ss_m};
+  if (a.ev_start || a.ev_stop)
+    return hipExtLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream, a.ev_start,
+                              a.ev_stop, 0);
   return hipLaunchKernel(f, grid, block, args, (size_t)a.lds_bytes, stream);
 }
 

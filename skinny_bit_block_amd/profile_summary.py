@@ -1,0 +1,208 @@
+"""Summaries of rocprofv3 runs of `bench.py --mode kernels`, per kernel and per
+(matrix shape, row count).
+
+bench.py --mode kernels --seq-out SEQ launches one event-timed eager pass per
+row count and two calls of each single-matrix workload per row count, and
+writes the sequence of its launches (kernel symbol, shape, M) to SEQ. The
+profiler's dispatches of the library's kernels come in the same order, so
+each one can be named by its shape and row count:
+
+  trace:    python -m skinny_bit_block_amd.profile_summary trace --csv <kernel_trace.csv>
+                --seq SEQ --command "..." --out profiles/kernels_trace_pass_and_configs.md
+  counters: python -m skinny_bit_block_amd.profile_summary counters --fetch <csv> --write <csv>
+                --copy-fetch <csv> --copy-write <csv> --seq SEQ --command "..."
+                --out profiles/counters_pass_and_configs.txt
+
+Counter bytes are calibrated against a plain device copy of known size (bench.py
+--mode copy, 1 GiB): FETCH_SIZE and WRITE_SIZE are scaled so that the copy
+reads and writes exactly its size. The counter summary ends with
+"traffic_bytes_per_dispatch[key]: bytes" lines (key = kernel symbol, "shape
+M=m" or "config shape M=m"), which bench.py reads back when the kernel source
+has not changed since, and it applies the accounting's counter guard (counter
+bytes below 0.98 x the weight bytes mean a cache served the weights).
+"""
+import argparse
+import csv
+import json
+import re
+import sys
+
+from . import accounting as acc
+
+_SYM = re.compile(r"(qmm_(?:vector|tiled)_kernel<[^>]*>)")
+
+
+def _col(row, *names):
+    low = {k.lower(): k for k in row}
+    for n in names:
+        if n.lower() in low:
+            return row[low[n.lower()]]
+    raise KeyError(names)
+
+
+def _symbol(name):
+    m = _SYM.search(name)
+    return m.group(1) if m else None
+
+
+def _dispatches(path):
+    """[(dispatch id, symbol, row)] of the library's kernels, in dispatch order."""
+    out = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            sym = _symbol(_col(row, "Kernel_Name", "KernelName"))
+            if sym:
+                out.append((int(_col(row, "Dispatch_Id", "Dispatch_ID", "DispatchId")), sym, row))
+    out.sort(key=lambda t: t[0])
+    return out
+
+
+def _align(disp, seq):
+    """Name each dispatch by its launch; the symbols must agree one by one."""
+    if len(disp) != len(seq):
+        raise SystemExit("%d library dispatches but %d launches in the sequence" % (len(disp), len(seq)))
+    for (did, sym, _), s in zip(disp, seq):
+        if sym != s["symbol"]:
+            raise SystemExit("dispatch %d is %s, the sequence has %s" % (did, sym, s["symbol"]))
+    return list(zip(disp, seq))
+
+
+def _key(s):
+    return "%s M=%d" % (s["shape"], s["M"])
+
+
+def trace(args):
+    seq = json.load(open(args.seq))
+    pairs = _align(_dispatches(args.csv), seq["launches"])
+    by_sym, by_key = {}, {}
+    for (did, sym, row), s in pairs:
+        us = (int(_col(row, "End_Timestamp", "EndNs")) - int(_col(row, "Start_Timestamp", "BeginNs"))) * 1e-3
+        for k, t in ((sym, by_sym), (_key(s), by_key)):
+            d = t.setdefault(k, {"n": 0, "us": 0.0, "wb": 0, "ab": 0, "min": 1e30, "max": 0.0})
+            d["n"] += 1
+            d["us"] += us
+            d["min"] = min(d["min"], us)
+            d["max"] = max(d["max"], us)
+            d["wb"] += acc.weight_bytes(s["N"], s["K"])
+            d["ab"] += acc.call_bytes(s["M"], s["N"], s["K"])
+    lines = ["# rocprofv3 kernel trace: event-timed eager launches of bench.py --mode kernels", "",
+             "command (repository root, after cd /tmp && export TMPDIR=/tmp):", "  " + args.command,
+             "kernel_source_sha256: %s" % seq["kernel_source_sha256"], "",
+             "Per kernel: algorithmic bytes per launch (weights + fp32 x + fp32 y) over the mean kernel",
+             "duration; the bench line's roofline divides the same bytes by its own event-timed mean.", "",
+             "| kernel | dispatches | mean us | min us | max us | algorithmic GB/s | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for k, d in sorted(by_sym.items()):
+        mean = d["us"] / d["n"]
+        gbs = d["ab"] / d["n"] / (mean * 1e-6) / 1e9
+        lines.append("| %s | %d | %.3f | %.3f | %.3f | %.1f | %.2f |"
+                     % (k, d["n"], mean, d["min"], d["max"], gbs, gbs / 80.0))
+    lines += ["", "Per shape and row count (weight bytes only):", "",
+              "| shape, M | dispatches | mean us | weight GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+    for k, d in sorted(by_key.items()):
+        mean = d["us"] / d["n"]
+        gbs = d["wb"] / d["n"] / (mean * 1e-6) / 1e9
+        lines.append("| %s | %d | %.3f | %.1f | %.2f |" % (k, d["n"], mean, gbs, gbs / 80.0))
+    for k, d in sorted(by_sym.items()):
+        lines.append("mean_kernel_us[%s]: %.3f" % (k, d["us"] / d["n"]))
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def _counter(path, name):
+    vals = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if _col(row, "Counter_Name", "CounterName") != name:
+                continue
+            did = int(_col(row, "Dispatch_Id", "Dispatch_ID", "DispatchId"))
+            vals[did] = vals.get(did, 0.0) + float(_col(row, "Counter_Value", "CounterValue"))
+    return vals
+
+
+def _copy_kib(path, name):
+    vals = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if "copyBuffer" in _col(row, "Kernel_Name", "KernelName") and \
+                    _col(row, "Counter_Name", "CounterName") == name:
+                vals.append(float(_col(row, "Counter_Value", "CounterValue")))
+    if not vals:
+        raise SystemExit("no copy dispatch with %s in %s" % (name, path))
+    return sum(vals) / len(vals)
+
+
+def counters(args):
+    seq = json.load(open(args.seq))
+    fetch = _counter(args.fetch, "FETCH_SIZE")
+    write = _counter(args.write, "WRITE_SIZE")
+    copy_bytes = 1 << 30
+    ff = copy_bytes / 1024.0 / _copy_kib(args.copy_fetch, "FETCH_SIZE")
+    wf = copy_bytes / 1024.0 / _copy_kib(args.copy_write, "WRITE_SIZE")
+    # the counter CSV has one row per (dispatch, counter): keep one entry per dispatch
+    seen, disp = set(), []
+    for did, sym, row in _dispatches(args.fetch):
+        if did not in seen:
+            seen.add(did)
+            disp.append((did, sym, row))
+    pairs = _align(disp, seq["launches"])
+    # the WRITE_SIZE run dispatches the same sequence: pair its library dispatches by position
+    wdisp = sorted({int(_col(r, "Dispatch_Id", "Dispatch_ID", "DispatchId")) for _, _, r in _dispatches(args.write)})
+    if len(wdisp) != len(disp):
+        raise SystemExit("%d library dispatches in the FETCH_SIZE run, %d in the WRITE_SIZE run"
+                         % (len(disp), len(wdisp)))
+    by = {}
+    guard = []
+    for i, ((did, sym, row), s) in enumerate(pairs):
+        fb = fetch[did] * 1024.0 * ff
+        wb_ = write[wdisp[i]] * 1024.0 * wf
+        for k in (sym, _key(s)):
+            d = by.setdefault(k, {"n": 0, "f": 0.0, "w": 0.0, "wb": 0, "ab": 0})
+            d["n"] += 1
+            d["f"] += fb
+            d["w"] += wb_
+            d["wb"] += acc.weight_bytes(s["N"], s["K"])
+            d["ab"] += acc.call_bytes(s["M"], s["N"], s["K"])
+        try:
+            acc.check_counter_bytes(fb, acc.weight_bytes(s["N"], s["K"]), what=_key(s))
+        except acc.RooflineViolation as e:
+            guard.append(str(e))
+    lines = ["# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+             "workload: bench.py --mode kernels (one eager pass at each M, two calls of each "
+             "single-matrix workload per M)",
+             "kernel_source_sha256: %s" % seq["kernel_source_sha256"],
+             "commands (repository root, after cd /tmp && export TMPDIR=/tmp):"]
+    lines += ["  " + c for c in args.command.split(" ;; ")]
+    lines += ["calibration (plain 1 GiB device copy): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (ff, wf),
+              "counter guard (counter bytes >= 0.98 x weight bytes per dispatch): %s"
+              % ("passed on every dispatch" if not guard else "FAILED: " + "; ".join(guard[:5])),
+              "",
+              "key | dispatches | fetch bytes | write bytes | traffic/dispatch | algorithmic/dispatch | ratio"]
+    for k, d in sorted(by.items()):
+        t = (d["f"] + d["w"]) / d["n"]
+        a = d["ab"] / d["n"]
+        lines.append("%s | %d | %.0f | %.0f | %.0f | %.0f | %.3f" % (k, d["n"], d["f"] / d["n"],
+                                                                      d["w"] / d["n"], t, a, t / a))
+    for k, d in sorted(by.items()):
+        lines.append("traffic_bytes_per_dispatch[%s]: %.0f" % (k, (d["f"] + d["w"]) / d["n"]))
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    if guard:
+        sys.stderr.write("counter guard failed on %d dispatches\n" % len(guard))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--csv", required=True)
+    t.add_argument("--seq", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--seq", "--command", "--out"):
+        c.add_argument(a, required=True)
+    args = ap.parse_args(argv)
+    {"trace": trace, "counters": counters}[args.what](args)
+
+
+if __name__ == "__main__":
+    main()

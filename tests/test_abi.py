@@ -11,10 +11,10 @@ import skinny_bit_block_amd as sbb
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "qmm.h")).read()
+def declared_functions(header="qmm.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*\**\s*\b(qmm_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*\**\s*\b(\w+)\s*\(", src, re.M)))
 
 
 def test_header_declarations_are_exported():
@@ -24,6 +24,22 @@ def test_header_declarations_are_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(sbb.EXPORTS) == names
+
+
+def test_every_header_is_exported():
+    # every function any header under include/ declares is exported by the
+    # library, and each header has a binding module listing exactly its names
+    from skinny_bit_block_amd import probe
+    lib = ctypes.CDLL(sbb.LIB_PATH)
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    listed = {"qmm.h": sbb.EXPORTS, "qmm_probe.h": probe.EXPORTS}
+    assert set(headers) <= set(listed), headers
+    for hname in headers:
+        names = declared_functions(hname)
+        assert names, hname
+        for n in names:
+            assert hasattr(lib, n), (hname, n)
+        assert sorted(listed[hname]) == names, hname
 
 
 def test_status_strings():
@@ -117,7 +133,10 @@ def test_overrides(planner):
     assert sbb.qmm_query_plan(planner, 1, 2048, 2048)["kernel"] == sbb.KERNEL_TILED
     assert sbb.qmm_query_plan(planner, 8, 2048, 2048)["kernel"] == sbb.KERNEL_TILED
     sbb.qmm_set_kernel(planner, sbb.KERNEL_VECTOR)
-    assert sbb.qmm_query_plan(planner, 16, 2048, 2048)["kernel"] == sbb.KERNEL_VECTOR
+    assert sbb.qmm_query_plan(planner, 8, 2048, 2048)["kernel"] == sbb.KERNEL_VECTOR
+    with pytest.raises(sbb.QmmError) as e:  # the row-vector kernel stops at 8 rows
+        sbb.qmm_query_plan(planner, 9, 2048, 2048)
+    assert e.value.status == sbb.QMM_ERR_INVALID_ARG
     sbb.qmm_set_kernel(planner, sbb.KERNEL_AUTO)
     sbb.qmm_set_shape(planner, 4, 2, 40)
     p = sbb.qmm_query_plan(planner, 4, 2048, 2048)

@@ -20,3 +20,11 @@ def test_parametrization_is_the_table():
     names = {p[0] for p in wc.params()}
     assert names == set(wc.CASES)
     assert t.WORKLOAD_PARAMS == wc.params()
+
+
+def test_every_fused_pass_call_has_a_parity_case():
+    # the fused-projection pass calls each layer's five same-input 5120x5120
+    # projections as one 25600-row matrix, the rest as in the full pass
+    shapes = {(5 * N, K) if N == K else (N, K) for _, N, K in acc.full_pass_shapes()} | {(5120, 5120)}
+    missing = sorted((N, K, M) for N, K in shapes for M in wc.PASS_ROWS if not wc.covered(N, K, M))
+    assert not missing, "fused-pass calls without a GPU parity case: %s" % missing

@@ -14,6 +14,8 @@ CASES = {
     "gate_up": (34816, 5120, [1, 2, 4, 7, 8, 9, 16, 32], 1.0),
     "down": (5120, 17408, [1, 4, 6, 8, 12, 16, 32], 0.1),
     "lm_head": (151936, 5120, [1, 4, 7, 8, 16, 32], 1.0),
+    # each layer's five same-input projections as one call (the fused-projection pass)
+    "fused_5x5120": (25600, 5120, [1, 4, 8, 16, 32], 1.0),
 }
 
 # rows of the timed full pass (the headline passes and the 32-row pass)
