@@ -38,7 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "weight GB/s (% HBM peak) and ms per 15.8 GB pass at M=1,4,8,16"
 PEAK_GBS = 8000.0
 SEED = 20261202
-KERNEL_SRC = os.path.join(ROOT, "skinny_bit_block_amd", "csrc", "qmm_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "skinny_bit_block_amd", "csrc", f)
+               for f in ("qmm_kernels.hip", "qmm_internal.h", "qmm_api.cpp")]
 
 
 def log(msg):
@@ -47,7 +48,12 @@ def log(msg):
 
 
 def kernel_source_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernels and the launch table: a profile taken on other source
+    does not describe these launches."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -272,9 +278,10 @@ def kernel_timing(P, M_list, seq=None):
     return sym, shp
 
 
-def read_profile(name):
-    """key -> value lines of a committed profile summary under profiles/, or {}
-    when it is absent or was taken on other kernel source."""
+def read_profile(name, field="traffic_bytes_per_dispatch"):
+    """key -> value of the "field[key]: value" lines of a committed profile
+    summary under profiles/, or {} when it is absent or was taken on other
+    kernel source."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return {}
@@ -282,8 +289,8 @@ def read_profile(name):
     for line in open(path):
         if line.startswith("kernel_source_sha256:"):
             sha = line.split(":", 1)[1].strip()
-        elif line.startswith("traffic_bytes_per_dispatch[") and "]:" in line:
-            key = line[len("traffic_bytes_per_dispatch["):line.index("]:")]
+        elif line.startswith(field + "[") and "]:" in line:
+            key = line[len(field) + 1:line.index("]:")]
             vals[key] = float(line.split("]:", 1)[1].strip())
     return vals if sha == kernel_source_sha() else {}
 
@@ -752,6 +759,11 @@ def mode_pass(args, torch, sbb, synth, acc):
                        "algorithmic_bytes_per_launch": round(bytes_per_launch, 0),
                        "timing": "kernel start to end (HIP events recorded by the launch itself), "
                                  "one eager pass per M in %s" % ms}
+    trace_us = read_profile("kernels_trace_pass_and_configs.md", "mean_kernel_us").get(dom)
+    if trace_us is not None:
+        # the committed rocprofv3 trace of the same launches (bench.py --mode kernels)
+        out["roofline"]["profile_avg_kernel_us"] = trace_us
+        out["roofline"]["frac_from_profile"] = round(bytes_per_launch / (trace_us * 1e-6) / 1e9 / PEAK_GBS, 4)
     if ceiling:
         out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
     out["kernels"] = {k: {"launches": v["launches"], "avg_us": round(v["us"] / v["launches"], 3),

@@ -8,7 +8,8 @@ profiler's dispatches of the library's kernels come in the same order, so
 each one can be named by its shape and row count:
 
   trace:    python -m skinny_bit_block_amd.profile_summary trace --csv <kernel_trace.csv>
-                --seq SEQ --command "..." --out profiles/kernels_trace_pass_and_configs.md
+                [--stats <kernel_stats.csv>] --seq SEQ --command "..."
+                --out profiles/kernels_trace_pass_and_configs.md
   counters: python -m skinny_bit_block_amd.profile_summary counters --fetch <csv> --write <csv>
                 --copy-fetch <csv> --copy-write <csv> --seq SEQ --command "..."
                 --out profiles/counters_pass_and_configs.txt
@@ -71,13 +72,19 @@ def _key(s):
     return "%s M=%d" % (s["shape"], s["M"])
 
 
+def _config(s):
+    # launches of the single-matrix workloads; the rest are the full passes
+    return s["shape"].startswith("config ")
+
+
 def trace(args):
     seq = json.load(open(args.seq))
     pairs = _align(_dispatches(args.csv), seq["launches"])
     by_sym, by_key = {}, {}
     for (did, sym, row), s in pairs:
         us = (int(_col(row, "End_Timestamp", "EndNs")) - int(_col(row, "Start_Timestamp", "BeginNs"))) * 1e-3
-        for k, t in ((sym, by_sym), (_key(s), by_key)):
+        keys = ((_key(s), by_key),) if _config(s) else ((sym, by_sym), (_key(s), by_key))
+        for k, t in keys:
             d = t.setdefault(k, {"n": 0, "us": 0.0, "wb": 0, "ab": 0, "min": 1e30, "max": 0.0})
             d["n"] += 1
             d["us"] += us
@@ -88,8 +95,9 @@ def trace(args):
     lines = ["# rocprofv3 kernel trace: event-timed eager launches of bench.py --mode kernels", "",
              "command (repository root, after cd /tmp && export TMPDIR=/tmp):", "  " + args.command,
              "kernel_source_sha256: %s" % seq["kernel_source_sha256"], "",
-             "Per kernel: algorithmic bytes per launch (weights + fp32 x + fp32 y) over the mean kernel",
-             "duration; the bench line's roofline divides the same bytes by its own event-timed mean.", "",
+             "Per kernel, over the launches of the full passes (one eager pass at each M): algorithmic",
+             "bytes per launch (weights + fp32 x + fp32 y) over the mean kernel duration. The bench",
+             "line's roofline divides the same bytes by its own event-timed mean of the same launches.", "",
              "| kernel | dispatches | mean us | min us | max us | algorithmic GB/s | % of 8 TB/s |",
              "|---|---|---|---|---|---|---|"]
     for k, d in sorted(by_sym.items()):
@@ -97,12 +105,24 @@ def trace(args):
         gbs = d["ab"] / d["n"] / (mean * 1e-6) / 1e9
         lines.append("| %s | %d | %.3f | %.3f | %.3f | %.1f | %.2f |"
                      % (k, d["n"], mean, d["min"], d["max"], gbs, gbs / 80.0))
-    lines += ["", "Per shape and row count (weight bytes only):", "",
+    lines += ["", "Per shape and row count (weight bytes only; \"config\" rows are the single-matrix",
+              "workloads, two calls on distinct copies per M):", "",
               "| shape, M | dispatches | mean us | weight GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
     for k, d in sorted(by_key.items()):
         mean = d["us"] / d["n"]
         gbs = d["wb"] / d["n"] / (mean * 1e-6) / 1e9
         lines.append("| %s | %d | %.3f | %.1f | %.2f |" % (k, d["n"], mean, gbs, gbs / 80.0))
+    if args.stats:
+        lines += ["", "rocprofv3 --stats of the same run (every dispatch of the program: the full passes",
+                  "and the single-matrix workloads together):", "",
+                  "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+        with open(args.stats) as f:
+            for row in csv.DictReader(f):
+                name = _symbol(row["Name"]) or row["Name"][:60]
+                lines.append("| %s | %s | %.3f | %.3f | %.3f | %.2f |" % (
+                    name, row["Calls"], float(row["AverageNs"]) * 1e-3, float(row["MinNs"]) * 1e-3,
+                    float(row["MaxNs"]) * 1e-3, float(row["Percentage"])))
+        lines.append("")
     for k, d in sorted(by_sym.items()):
         lines.append("mean_kernel_us[%s]: %.3f" % (k, d["us"] / d["n"]))
     open(args.out, "w").write("\n".join(lines) + "\n")
@@ -155,7 +175,7 @@ def counters(args):
     for i, ((did, sym, row), s) in enumerate(pairs):
         fb = fetch[did] * 1024.0 * ff
         wb_ = write[wdisp[i]] * 1024.0 * wf
-        for k in (sym, _key(s)):
+        for k in ((_key(s),) if _config(s) else (sym, _key(s))):
             d = by.setdefault(k, {"n": 0, "f": 0.0, "w": 0.0, "wb": 0, "ab": 0})
             d["n"] += 1
             d["f"] += fb
@@ -176,6 +196,7 @@ def counters(args):
               "counter guard (counter bytes >= 0.98 x weight bytes per dispatch): %s"
               % ("passed on every dispatch" if not guard else "FAILED: " + "; ".join(guard[:5])),
               "",
+              "(kernel keys: the full-pass launches; \"config\" keys: the single-matrix workloads)",
               "key | dispatches | fetch bytes | write bytes | traffic/dispatch | algorithmic/dispatch | ratio"]
     for k, d in sorted(by.items()):
         t = (d["f"] + d["w"]) / d["n"]
@@ -197,6 +218,7 @@ def main(argv=None):
     t.add_argument("--seq", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--stats", default="", help="rocprofv3's kernel_stats.csv of the same run")
     c = sub.add_parser("counters")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--seq", "--command", "--out"):
         c.add_argument(a, required=True)

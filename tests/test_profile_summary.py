@@ -1,0 +1,127 @@
+"""The rocprofv3 summary tool on synthetic CSVs, and the counter guard applied
+to the committed counter summary."""
+import csv
+import json
+import os
+import re
+
+import pytest
+
+from skinny_bit_block_amd import accounting as acc
+from skinny_bit_block_amd import profile_summary as ps
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SHAPES = {"square": (5120, 5120), "gate_up": (34816, 5120), "down": (5120, 17408),
+          "lm_head": (151936, 5120), "single_2048": (2048, 2048)}
+
+
+def _seq():
+    launches = []
+    for M in (1, 4):
+        sym = "qmm_vector_kernel<1>" if M == 1 else "qmm_tiled_kernel<1, false, 0>"
+        for shape in ("square", "square", "gate_up", "down", "lm_head"):
+            N, K = SHAPES[shape]
+            launches.append({"symbol": sym, "shape": shape, "M": M, "N": N, "K": K})
+    launches.append({"symbol": "qmm_tiled_kernel<1, false, 0>", "shape": "config single_2048",
+                     "M": 4, "N": 2048, "K": 2048})
+    return {"kernel_source_sha256": "0123456789abcdef", "launches": launches}
+
+
+def _write_trace(path, seq):
+    cols = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        did, t = 1, 1000
+        for i, s in enumerate(seq["launches"]):
+            # a foreign kernel between the library's dispatches is ignored
+            w.writerow(["KERNEL_DISPATCH", did, "void qmm::zero_u32(unsigned int*, int)", t, t + 500])
+            did += 1
+            us = acc.weight_bytes(s["N"], s["K"]) / 4e3  # 4 TB/s
+            w.writerow(["KERNEL_DISPATCH", did, "void qmm::%s(qmm::Args)" % s["symbol"],
+                        t, t + int(us * 1000)])
+            did += 1
+            t += 10 ** 6
+
+
+def _write_counter(path, seq, name, scale, copy_kib=None):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        did = 7
+        if copy_kib is not None:
+            for _ in range(3):
+                w.writerow([did, "__amd_rocclr_copyBuffer", name, copy_kib])
+                did += 1
+            return
+        for s in seq["launches"]:
+            b = acc.weight_bytes(s["N"], s["K"]) if name == "FETCH_SIZE" else 4 * s["M"] * s["N"]
+            # two counter instances per dispatch (summed by the tool)
+            w.writerow([did, "void qmm::%s(qmm::Args)" % s["symbol"], name, b / 1024.0 / scale / 2])
+            w.writerow([did, "void qmm::%s(qmm::Args)" % s["symbol"], name, b / 1024.0 / scale / 2])
+            did += 3
+
+
+def test_trace_summary(tmp_path):
+    seq = _seq()
+    json.dump(seq, open(tmp_path / "seq.json", "w"))
+    _write_trace(tmp_path / "t.csv", seq)
+    ps.main(["trace", "--csv", str(tmp_path / "t.csv"), "--seq", str(tmp_path / "seq.json"),
+             "--command", "cmd", "--out", str(tmp_path / "t.md")])
+    text = open(tmp_path / "t.md").read()
+    assert "kernel_source_sha256: 0123456789abcdef" in text
+    means = dict(re.findall(r"mean_kernel_us\[(.+?)\]: ([\d.]+)", text))
+    # the config launch is not part of the kernel's full-pass mean
+    tiled = [acc.weight_bytes(*SHAPES[s]) / 4e3 for s in ("square", "square", "gate_up", "down", "lm_head")]
+    assert float(means["qmm_tiled_kernel<1, false, 0>"]) == pytest.approx(sum(tiled) / 5, abs=2e-3)
+    assert "| config single_2048 M=4 | 1 |" in text
+    assert "| square M=1 | 2 |" in text
+
+
+def test_trace_summary_rejects_a_mismatch(tmp_path):
+    seq = _seq()
+    _write_trace(tmp_path / "t.csv", seq)
+    seq["launches"][3]["symbol"] = "qmm_vector_kernel<4>"
+    json.dump(seq, open(tmp_path / "seq.json", "w"))
+    with pytest.raises(SystemExit):
+        ps.main(["trace", "--csv", str(tmp_path / "t.csv"), "--seq", str(tmp_path / "seq.json"),
+                 "--command", "cmd", "--out", str(tmp_path / "t.md")])
+
+
+def test_counter_summary_calibrates_and_guards(tmp_path):
+    seq = _seq()
+    json.dump(seq, open(tmp_path / "seq.json", "w"))
+    # the counters read half the bytes (FETCH_SIZE) / all of them (WRITE_SIZE)
+    _write_counter(tmp_path / "f.csv", seq, "FETCH_SIZE", 2.0)
+    _write_counter(tmp_path / "w.csv", seq, "WRITE_SIZE", 1.0)
+    _write_counter(tmp_path / "cf.csv", seq, "FETCH_SIZE", 1.0, copy_kib=(1 << 30) / 1024 / 2)
+    _write_counter(tmp_path / "cw.csv", seq, "WRITE_SIZE", 1.0, copy_kib=(1 << 30) / 1024)
+    ps.main(["counters", "--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
+             "--copy-fetch", str(tmp_path / "cf.csv"), "--copy-write", str(tmp_path / "cw.csv"),
+             "--seq", str(tmp_path / "seq.json"), "--command", "a ;; b", "--out", str(tmp_path / "c.txt")])
+    text = open(tmp_path / "c.txt").read()
+    assert "FETCH_SIZE x 2.0000, WRITE_SIZE x 1.0000" in text
+    assert "passed on every dispatch" in text
+    t = dict(re.findall(r"traffic_bytes_per_dispatch\[(.+?)\]: (\d+)", text))
+    N, K = SHAPES["lm_head"]
+    assert int(t["lm_head M=4"]) == pytest.approx(acc.weight_bytes(N, K) + 4 * 4 * N, abs=1)
+    assert "config single_2048 M=4" in t
+
+
+def test_committed_counters_pass_the_guard():
+    # every full-pass and workload dispatch read at least 0.98 x its weight bytes
+    path = os.path.join(ROOT, "profiles", "counters_pass_and_configs.txt")
+    if not os.path.exists(path):
+        pytest.skip("no committed counter summary")
+    text = open(path).read()
+    assert "passed on every dispatch" in text
+    checked = 0
+    for key, val in re.findall(r"traffic_bytes_per_dispatch\[(.+?)\]: (\d+)", text):
+        m = re.match(r"(?:config )?(\w+) M=(\d+)$", key)
+        if not m:
+            continue
+        N, K = SHAPES[m.group(1)]
+        acc.check_counter_bytes(float(val), acc.weight_bytes(N, K), what=key)
+        checked += 1
+    assert checked >= 20
