@@ -251,6 +251,24 @@ typedef struct {
  * overrides. Returns a status like qmm_run's argument checks. */
 int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out);
 
+/* Weight formats of the entry points: qmm_run / qmm_run_ids (4.5-bit
+ * super-blocks), qmm_run_nvfp4, qmm_run_int4. */
+enum {
+  QMM_FORMAT_KQUANT = 0,
+  QMM_FORMAT_NVFP4 = 1,
+  QMM_FORMAT_INT4 = 2
+};
+
+/* The entry the call of that format would use, with the handle's current
+ * overrides: expert_slots = 0 for a plain call, else the distinct experts an
+ * expert-indexed call (qmm_run_ids) holds in its grid, min(M, E). For tests
+ * that replay the kernels' index arithmetic on the host, and for sweeps.
+ * QMM_ERR_INVALID_ARG for an unknown format, expert slots with a format other
+ * than QMM_FORMAT_KQUANT, or slots outside 0..M; otherwise like
+ * qmm_query_plan. */
+int qmm_query_plan_format(qmm_handle h, int format, int expert_slots, int64_t M, int64_t N,
+                          int64_t K, qmm_plan* out);
+
 /* Force a kernel for every following call on this handle (QMM_KERNEL_AUTO
  * restores the table). For tests and sweeps. A call that forces the
  * row-vector kernel above 8 rows returns QMM_ERR_INVALID_ARG. */

@@ -27,12 +27,13 @@ QMM_MAX_M = 32
 QMM_DEVICE_NONE = -1  # planning-only handle: plans and checks arguments, never launches
 
 KERNEL_AUTO, KERNEL_VECTOR, KERNEL_TILED = 0, 1, 2
+FORMAT_KQUANT, FORMAT_NVFP4, FORMAT_INT4 = 0, 1, 2
 KERNEL_NAMES = {KERNEL_VECTOR: "vector", KERNEL_TILED: "tiled"}
 
 EXPORTS = ["qmm_create", "qmm_run", "qmm_run_static", "qmm_run_ids", "qmm_run_nvfp4", "qmm_nvfp4_repack",
            "qmm_run_int4", "qmm_int4_repack", "qmm_destroy", "qmm_status_string", "qmm_weight_bytes",
            "qmm_query_plan", "qmm_set_kernel", "qmm_set_shape", "qmm_set_wave_splits",
-           "qmm_switch_point", "qmm_set_launch_events"]
+           "qmm_switch_point", "qmm_set_launch_events", "qmm_query_plan_format"]
 
 
 class qmm_plan(ctypes.Structure):
@@ -81,6 +82,9 @@ def load():
         lib.qmm_weight_bytes.restype = ctypes.c_uint64
         lib.qmm_query_plan.argtypes = [vp, i64, i64, i64, ctypes.POINTER(qmm_plan)]
         lib.qmm_query_plan.restype = ctypes.c_int
+        lib.qmm_query_plan_format.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                              ctypes.POINTER(qmm_plan)]
+        lib.qmm_query_plan_format.restype = ctypes.c_int
         lib.qmm_set_kernel.argtypes = [vp, ctypes.c_int]
         lib.qmm_set_kernel.restype = ctypes.c_int
         lib.qmm_set_shape.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -301,6 +305,13 @@ def qmm_run_raw(h, x_ptr, w_ptr, y_ptr, M, N, K, stream_ptr):
 def qmm_query_plan(h, M, N, K):
     p = qmm_plan()
     _check(load().qmm_query_plan(h, int(M), int(N), int(K), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def qmm_query_plan_format(h, fmt, expert_slots, M, N, K):
+    p = qmm_plan()
+    _check(load().qmm_query_plan_format(h, int(fmt), int(expert_slots), int(M), int(N), int(K),
+                                        ctypes.byref(p)))
     return p.as_dict()
 
 

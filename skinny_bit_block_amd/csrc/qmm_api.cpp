@@ -374,6 +374,14 @@ int qmm_query_plan(qmm_handle h, int64_t M, int64_t N, int64_t K, qmm_plan* out)
   return make_plan(h, M, N, K, out);
 }
 
+int qmm_query_plan_format(qmm_handle h, int format, int expert_slots, int64_t M, int64_t N,
+                          int64_t K, qmm_plan* out) {
+  if (!h || !out || format < QMM_FORMAT_KQUANT || format > QMM_FORMAT_INT4 || expert_slots < 0 ||
+      (expert_slots > 0 && (format != QMM_FORMAT_KQUANT || expert_slots > M)))
+    return QMM_ERR_INVALID_ARG;
+  return make_plan(h, M, N, K, out, expert_slots, format);
+}
+
 int qmm_set_kernel(qmm_handle h, int kernel) {
   if (!h || kernel < QMM_KERNEL_AUTO || kernel > QMM_KERNEL_TILED) return QMM_ERR_INVALID_ARG;
   h->forced_kernel = kernel;
