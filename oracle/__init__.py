@@ -12,6 +12,10 @@ oracle.nvfp4 is the oracle of the block-scaled FP4 product (numpy, binary64;
 its header gives the format's sources and pins).
 oracle.int4 is the oracle of the plain 4-bit integer product, one binary16
 scale per 128 columns (numpy, binary64; its header gives the reading and pins).
+oracle.gdn is the oracle of the Gated DeltaNet recurrent update with the
+replay of a row log (numpy, binary64; parity unpinned against the pages, which
+give the update's inputs but not its equation; its header gives the source and
+the pins).
 """
 import ctypes
 import os

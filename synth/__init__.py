@@ -27,6 +27,9 @@ DEFAULT_SEED = 20261202
 BLOCK_BYTES = 144
 BLOCK_WEIGHTS = 256
 FIELD_BYTES, FIELD_D, FIELD_DMIN, FIELD_X, FIELD_FP4_ELEMS, FIELD_FP4_SCALES = 1, 2, 3, 4, 5, 6
+# streams of the recurrent-update inputs
+(FIELD_GDN_STATE, FIELD_GDN_Q, FIELD_GDN_K, FIELD_GDN_V, FIELD_GDN_GATE,
+ FIELD_GDN_BETA) = 16, 17, 18, 19, 20, 21
 
 
 def build():
@@ -58,6 +61,13 @@ def _load():
         lib.synth_int4.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_int4.restype = ctypes.c_int
+        lib.synth_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                         ctypes.c_int64, ctypes.c_double, ctypes.c_void_p]
+        lib.synth_normal_f32.restype = ctypes.c_int
+        lib.synth_uniform_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                                          ctypes.c_void_p]
+        lib.synth_uniform_f32.restype = ctypes.c_int
         lib.synth_f64_to_f16.argtypes = [ctypes.c_double]
         lib.synth_f64_to_f16.restype = ctypes.c_uint16
         lib.synth_word.argtypes = [ctypes.c_uint64] * 4
@@ -129,6 +139,56 @@ def int4(n_rows, K, tensor, seed=DEFAULT_SEED):
     if rc:
         raise RuntimeError("synth_int4 failed")
     return codes, scales
+
+
+def normal_f32(n, tensor, field, seed=DEFAULT_SEED, scale=1.0):
+    """fp32 [n], f32(scale * z), z ~ N(0,1), of stream (seed, tensor, field)."""
+    out = np.empty(int(n), dtype=np.float32)
+    if _load().synth_normal_f32(seed, tensor, field, int(n), float(scale), out.ctypes.data):
+        raise RuntimeError("synth_normal_f32 failed")
+    return out
+
+
+def uniform_f32(n, tensor, field, lo, hi, seed=DEFAULT_SEED):
+    """fp32 [n], f32(lo + (hi - lo) * w), w uniform in [0, 1) (53 bits)."""
+    out = np.empty(int(n), dtype=np.float32)
+    if _load().synth_uniform_f32(seed, tensor, field, int(n), float(lo), float(hi), out.ctypes.data):
+        raise RuntimeError("synth_uniform_f32 failed")
+    return out
+
+
+def _unit_rows(a, scale=1.0):
+    # rows of a rescaled to Euclidean norm `scale` (binary64), rounded to fp32
+    a64 = a.astype(np.float64)
+    n = np.sqrt((a64 * a64).sum(axis=-1, keepdims=True))
+    return (scale * a64 / np.where(n > 0, n, 1.0)).astype(np.float32)
+
+
+def gdn_rows(B, R, H, dk, dv, tensor, seed=DEFAULT_SEED, queries=True):
+    """Per-row inputs of the recurrent update for B sequences of R rows and H
+    heads: dict of q [B,R,H,dk] (unit norm times dk^-1/2; omitted when
+    queries is False), k [B,R,H,dk] (unit norm), v [B,R,H,dv] ~ N(0,1),
+    gate [B,R,H] uniform in [0.85, 1), beta [B,R,H] uniform in [0.05, 0.95).
+    The shapes and distributions of a Gated DeltaNet layer's inputs after its
+    key/query normalization; no trained weights."""
+    out = {}
+    shape = (B, R, H)
+    n = B * R * H
+    if queries:
+        out["q"] = _unit_rows(normal_f32(n * dk, tensor, FIELD_GDN_Q, seed).reshape(shape + (dk,)),
+                              dk ** -0.5)
+    out["k"] = _unit_rows(normal_f32(n * dk, tensor, FIELD_GDN_K, seed).reshape(shape + (dk,)))
+    out["v"] = normal_f32(n * dv, tensor, FIELD_GDN_V, seed).reshape(shape + (dv,))
+    out["gate"] = uniform_f32(n, tensor, FIELD_GDN_GATE, 0.85, 1.0, seed).reshape(shape)
+    out["beta"] = uniform_f32(n, tensor, FIELD_GDN_BETA, 0.05, 0.95, seed).reshape(shape)
+    return out
+
+
+def gdn_state(B, H, dk, dv, tensor, seed=DEFAULT_SEED, scale=0.05):
+    """Base states [B,H,dk,dv] fp32, f32(scale * z): the layout keeps the key
+    index outer and the value index inner (element [b,h,e,i] is row i, column
+    e of the head's value-by-key state matrix)."""
+    return normal_f32(B * H * dk * dv, tensor, FIELD_GDN_STATE, seed, scale).reshape(B, H, dk, dv)
 
 
 def f64_to_f16_bits(v):

@@ -170,6 +170,29 @@ int synth_acts(uint64_t seed, uint64_t tensor, int64_t M, int64_t K, double scal
   return 0;
 }
 
+/* n values f32_rne(scale * z), z ~ N(0,1), of stream `field` (generic inputs). */
+int synth_normal_f32(uint64_t seed, uint64_t tensor, uint64_t field, int64_t n, double scale,
+                     float* out) {
+  if (n < 0 || (n && !out)) return -1;
+  const uint64_t key = sm_key(seed, tensor, field);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)(scale * sm_normal(key, (uint64_t)i));
+  return 0;
+}
+
+/* n values f32_rne(lo + (hi - lo) * w), w = (53 high bits of the word) / 2^53 in [0, 1). */
+int synth_uniform_f32(uint64_t seed, uint64_t tensor, uint64_t field, int64_t n, double lo,
+                      double hi, float* out) {
+  if (n < 0 || (n && !out)) return -1;
+  const uint64_t key = sm_key(seed, tensor, field);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const double w = (double)(sm_word(key, (uint64_t)i) >> 11) * 0x1.0p-53;
+    out[i] = (float)(lo + (hi - lo) * w);
+  }
+  return 0;
+}
+
 /* Raw stream access, used by the tests of the generator itself. */
 uint64_t synth_word(uint64_t seed, uint64_t tensor, uint64_t field, uint64_t i) {
   return sm_word(sm_key(seed, tensor, field), i);
