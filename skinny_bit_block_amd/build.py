@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmm.so")
-SOURCES = ["qmm_kernels.hip", "qmm_api.cpp", "qmm_probe.hip"]
+SOURCES = ["qmm_kernels.hip", "qmm_api.cpp", "qmm_probe.hip", "gdn_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,280 @@
+// Gated DeltaNet recurrent update with the replay of a row log
+// (include/gdn.h): one base state per sequence, the kept rows of its log and
+// its new rows applied in one kernel ("sixi-asi 0.11", section "A log instead
+// of snapshots"); the update is the gated delta rule of the Gated DeltaNet
+// paper (Yang, Kautz and Hatamizadeh, ICLR 2025).
+//
+// Work split. Row i of a head's state evolves on its own given the row's
+// inputs: s <- alpha s + beta (v_i - alpha (s . k)) k, o_i = s . q. So one
+// lane owns one value row for the whole walk: its 128 state values stay in
+// VGPRs from the first row to the last (the state is read once and written at
+// most once per call, which is the HBM traffic of the step), the dot products
+// are lane-local (no cross-lane reduction), and everything else a row needs
+// (key, query, gate, beta) is the same for every lane of the wave: uniform
+// loads through the scalar cache whose values are SGPR operands of the
+// per-element FMAs. A wave holds 64 of a head's 128 value rows; the state
+// layout [B][H][dk][dv] puts those 64 rows' values of one key index in one
+// contiguous 256-byte run, so every state load and store is coalesced.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "../../include/qmm.h"
+
+namespace {
+
+constexpr int kDk = 128;
+constexpr int kDv = 128;
+constexpr int kWaveRows = 64;                   // value rows of a head per wave
+constexpr int kWavesPerHead = kDv / kWaveRows;  // 2
+
+// The inputs every lane of a wave reads alike (keys, queries, gates, betas)
+// are read through the constant address space: the call never writes them
+// (the host checks that no input overlaps the state or o), and loads from it
+// become scalar loads whatever the walk stores to o and to the state (through
+// a global pointer the compiler cannot prove that after the commit's 128
+// stores and falls back to vector loads of the uniform data).
+typedef __attribute__((address_space(4))) const float cfloat;
+
+// Inputs of one call as one wave walks them.
+struct Walk {
+  cfloat* k_log;
+  const float* __restrict__ v_log;
+  cfloat* g_log;
+  cfloat* b_log;
+  cfloat* q;
+  cfloat* k;
+  const float* __restrict__ v;
+  cfloat* g;
+  cfloat* beta;
+  float* __restrict__ o;
+  int b, h, H, M, L, nl, T, i;
+};
+
+// Row r of the walk: a kept row of the log (r < nl) or new row r - nl.
+struct RowRef {
+  cfloat* k;
+  float vi, alpha, beta;
+  bool fresh;
+  size_t row;  // index of the row's (b, row, h) entries
+};
+
+__device__ __forceinline__ RowRef row_ref(const Walk& w, int r) {
+  RowRef x;
+  x.fresh = r >= w.nl;
+  x.row = x.fresh ? ((size_t)w.b * w.M + (r - w.nl)) * w.H + w.h
+                  : ((size_t)w.b * w.L + r) * w.H + w.h;
+  x.k = (x.fresh ? w.k : w.k_log) + x.row * kDk;
+  x.vi = (x.fresh ? w.v : w.v_log)[x.row * kDv + w.i];
+  x.alpha = (x.fresh ? w.g : w.g_log)[x.row];
+  x.beta = (x.fresh ? w.beta : w.b_log)[x.row];
+  return x;
+}
+
+// s . kr over the lane's 128 state values, in four interleaved partial sums
+// (a fixed order: calls are bitwise repeatable)
+__device__ __forceinline__ float dot128(const float (&s)[kDk], cfloat* kr) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int e = 0; e < kDk; e += 4) {
+    a0 = __builtin_fmaf(s[e], kr[e], a0);
+    a1 = __builtin_fmaf(s[e + 1], kr[e + 1], a1);
+    a2 = __builtin_fmaf(s[e + 2], kr[e + 2], a2);
+    a3 = __builtin_fmaf(s[e + 3], kr[e + 3], a3);
+  }
+  return (a0 + a1) + (a2 + a3);
+}
+
+// The lane keeps its state row as s = P * z: P the product of the gates
+// applied since the last fold (wave-uniform) and z in registers. A row then
+// changes z by one FMA per element, z <- z + (u / P') k with P' = alpha P
+// (the decay is the scalar P' instead of 128 multiplies) and s . w = P (z . w).
+// z is folded (z <- P z, P <- 1) after any row that takes P below 2^-64,
+// which a scan of the gates finds before the rows run, and P' is kept at or
+// above 2^-100: a gate small enough to hit that floor decays the old state
+// by 2^-100 instead of less, a relative error of at most 2^-36 (the fold came
+// at most 2^64 earlier). Everything else is the row's update rounded in
+// binary32, so the error allowance per row is that of the plain update.
+constexpr float kFold = 0x1.0p-64f;
+constexpr float kFloor = 0x1.0p-100f;
+
+// The scaled gate product after a row, kept at or above the floor.
+__device__ __forceinline__ float next_scale(float P, float alpha) {
+  return __builtin_fmaxf(P * alpha, kFloor);
+}
+
+// Rows [r0, r1) of the walk, all of them kept rows of the log (OUT = false)
+// or all new rows (OUT = true, each followed by its output). One pass over
+// the lane's z per row: the update, and in the same pass the dot of the new z
+// with the next row's key (and with q_r for a new row).
+template <bool OUT>
+__device__ __forceinline__ void walk_rows(const Walk& w, float (&z)[kDk], float& P, RowRef& cur,
+                                          float& a, int r0, int r1) {
+  for (int r = r0; r < r1; ++r) {
+    const float u = cur.beta * (cur.vi - cur.alpha * a);  // a = s . k_r
+    const float Pn = next_scale(P, cur.alpha);
+    const float coef = u / Pn;
+    // the next row's key (the last row dots with its own key; the result is unused)
+    const RowRef nxt = row_ref(w, r + 1 < w.T ? r + 1 : r);
+    cfloat* kr = cur.k;
+    cfloat* kn = nxt.k;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    cfloat* qr = w.q + (OUT ? cur.row * kDk : 0);
+#pragma unroll
+    for (int e = 0; e < kDk; e += 4) {
+      z[e] = __builtin_fmaf(coef, kr[e], z[e]);
+      z[e + 1] = __builtin_fmaf(coef, kr[e + 1], z[e + 1]);
+      z[e + 2] = __builtin_fmaf(coef, kr[e + 2], z[e + 2]);
+      z[e + 3] = __builtin_fmaf(coef, kr[e + 3], z[e + 3]);
+      if (OUT) {
+        o0 = __builtin_fmaf(z[e], qr[e], o0);
+        o1 = __builtin_fmaf(z[e + 1], qr[e + 1], o1);
+        o2 = __builtin_fmaf(z[e + 2], qr[e + 2], o2);
+        o3 = __builtin_fmaf(z[e + 3], qr[e + 3], o3);
+      }
+      a0 = __builtin_fmaf(z[e], kn[e], a0);
+      a1 = __builtin_fmaf(z[e + 1], kn[e + 1], a1);
+      a2 = __builtin_fmaf(z[e + 2], kn[e + 2], a2);
+      a3 = __builtin_fmaf(z[e + 3], kn[e + 3], a3);
+    }
+    if (OUT) w.o[cur.row * kDv + w.i] = Pn * ((o0 + o1) + (o2 + o3));
+    a = Pn * ((a0 + a1) + (a2 + a3));
+    P = Pn;
+    cur = nxt;
+  }
+}
+
+// The first row after r at which the walk must fold z: the row after the
+// first one that takes the scaled gate product (P at row r) below 2^-64, or
+// `stop`. The same products as the walk's, so the walk's P after that row is
+// below 2^-64 too.
+__device__ __forceinline__ int fold_point(const Walk& w, int r, int stop, float P) {
+  float p = P;
+  for (int e = r; e < stop; ++e) {
+    const bool fresh = e >= w.nl;
+    const size_t row = fresh ? ((size_t)w.b * w.M + (e - w.nl)) * w.H + w.h
+                             : ((size_t)w.b * w.L + e) * w.H + w.h;
+    p = next_scale(p, (fresh ? w.g : w.g_log)[row]);
+    if (p < kFold) return e + 1;
+  }
+  return stop;
+}
+
+// One workgroup = one wave = 64 value rows of one head of one sequence:
+// blockIdx.x = (b * H + h) * 2 + half.
+__global__ void __launch_bounds__(64) gdn_replay_kernel(
+    float* __restrict__ state, const float* __restrict__ k_log, const float* __restrict__ v_log,
+    const float* __restrict__ g_log, const float* __restrict__ b_log,
+    const int32_t* __restrict__ n_log, int L, const float* __restrict__ q,
+    const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, const int32_t* __restrict__ commit, float* __restrict__ o,
+    int M, int H) {
+  const int lane = (int)threadIdx.x;
+  const int wg = (int)blockIdx.x;
+  const int half = wg % kWavesPerHead;
+  const int bh = wg / kWavesPerHead;
+  const int h = bh % H, b = bh / H;
+  const int i = half * kWaveRows + lane;  // this lane's value row
+
+  // the head's state (a wave-uniform base) and this lane's 32-bit offset
+  float* const head = state + (size_t)bh * kDk * kDv;
+  float z[kDk];
+#pragma unroll
+  for (int e = 0; e < kDk; ++e) z[e] = head[e * kDv + i];
+  float P = 1.f;
+
+  int nl = n_log ? n_log[b] : 0;
+  nl = nl < 0 ? 0 : (nl > L ? L : nl);
+  const int T = nl + M;
+  int c = commit ? commit[b] : 0;
+  c = c < 0 ? 0 : (c > T ? T : c);
+  if (T == 0) return;
+
+  const Walk w{(cfloat*)k_log, v_log, (cfloat*)g_log, (cfloat*)b_log, (cfloat*)q, (cfloat*)k, v,
+               (cfloat*)g, (cfloat*)beta, o, b, h, H, M, L, nl, T, i};
+  RowRef cur = row_ref(w, 0);
+  float a = dot128(z, cur.k);  // s . k of the current row (P = 1)
+  // segments of the walk end at the commit point, at fold points and at T
+  for (int r = 0; r < T;) {
+    const int end = fold_point(w, r, r < c ? c : T, P);
+    walk_rows<false>(w, z, P, cur, a, r, end < nl ? end : nl);
+    walk_rows<true>(w, z, P, cur, a, r > nl ? r : nl, end);
+    r = end;
+    if (P < kFold) {  // fold
+#pragma unroll
+      for (int e = 0; e < kDk; ++e) z[e] *= P;
+      P = 1.f;
+    }
+    if (r == c) {
+      // the commit's store takes an opaque copy of the lane offset: its
+      // addresses are formed here, not kept live from the loads at the top
+      int li = i;
+      asm("" : "+v"(li));
+#pragma unroll
+      for (int e = 0; e < kDk; ++e) head[e * kDv + li] = P * z[e];
+    }
+  }
+}
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_replay_update(float* state, const float* k_log, const float* v_log,
+                      const float* gate_log, const float* beta_log, const int32_t* n_log,
+                      int64_t L, const float* q, const float* k, const float* v,
+                      const float* gate, const float* beta, const int32_t* commit, float* o,
+                      int64_t B, int64_t M, int64_t H, int64_t dk, int64_t dv,
+                      hipStream_t stream) {
+  if (!state || B < 1 || H < 1 || M < 0 || L < 0) return QMM_ERR_INVALID_ARG;
+  if (dk != kDk || dv != kDv) return QMM_ERR_SHAPE;
+  if (L > 0 && (!k_log || !v_log || !gate_log || !beta_log || !n_log)) return QMM_ERR_INVALID_ARG;
+  if (M > 0 && (!q || !k || !v || !gate || !beta || !o)) return QMM_ERR_INVALID_ARG;
+  if (B > INT32_MAX / H || B * H > INT32_MAX / kWavesPerHead || L > INT32_MAX || M > INT32_MAX)
+    return QMM_ERR_INVALID_ARG;
+  const int64_t wgs = B * H * kWavesPerHead;
+  const void* ptrs[] = {state, k_log, v_log, gate_log, beta_log, n_log, q, k, v, gate, beta, commit, o};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 3) return QMM_ERR_ALIGN;
+  const uint64_t f = 4;
+  const uint64_t sb = (uint64_t)B * H * kDk * kDv * f;
+  const uint64_t lrow = (uint64_t)B * L * H, nrow = (uint64_t)B * M * H;
+  struct Arr {
+    const void* p;
+    uint64_t n;
+  };
+  const Arr ins[] = {{k_log, lrow * kDk * f}, {v_log, lrow * kDv * f}, {gate_log, lrow * f},
+                     {beta_log, lrow * f},    {n_log, L > 0 ? (uint64_t)B * 4 : 0},
+                     {q, nrow * kDk * f},     {k, nrow * kDk * f},   {v, nrow * kDv * f},
+                     {gate, nrow * f},        {beta, nrow * f},      {commit, commit ? (uint64_t)B * 4 : 0}};
+  const uint64_t ob = nrow * kDv * f;
+  if (overlaps(state, sb, o, ob)) return QMM_ERR_OVERLAP;
+  for (const Arr& a : ins)
+    if (overlaps(state, sb, a.p, a.n) || overlaps(o, ob, a.p, a.n)) return QMM_ERR_OVERLAP;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QMM_ERR_NO_DEVICE;
+  hipLaunchKernelGGL(gdn_replay_kernel, dim3((unsigned)wgs), dim3(kWaveRows), 0, stream, state,
+                     k_log, v_log, gate_log, beta_log, L > 0 ? n_log : nullptr, (int)L, q, k, v,
+                     gate, beta, commit, o, (int)M, (int)H);
+  return hipGetLastError() == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+uint64_t gdn_call_bytes(int64_t B, int64_t M, int64_t H, int64_t dk, int64_t dv,
+                        int64_t log_rows, int64_t committing) {
+  if (B < 0 || M < 0 || H < 0 || dk < 0 || dv < 0 || log_rows < 0 || committing < 0) return 0;
+  const uint64_t f = 4, head = (uint64_t)dk * dv * f;
+  const uint64_t states = (uint64_t)B * H * head + (uint64_t)committing * H * head;
+  const uint64_t logs = (uint64_t)log_rows * H * (dk + dv + 2) * f;
+  const uint64_t fresh = (uint64_t)B * M * H * (2 * dk + dv + 2) * f;
+  const uint64_t outs = (uint64_t)B * M * H * dv * f;
+  return states + logs + fresh + outs;
+}
+
+}  // extern "C"

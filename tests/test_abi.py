@@ -29,10 +29,10 @@ def test_header_declarations_are_exported():
 def test_every_header_is_exported():
     # every function any header under include/ declares is exported by the
     # library, and each header has a binding module listing exactly its names
-    from skinny_bit_block_amd import probe
+    from skinny_bit_block_amd import gdn, probe
     lib = ctypes.CDLL(sbb.LIB_PATH)
     headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
-    listed = {"qmm.h": sbb.EXPORTS, "qmm_probe.h": probe.EXPORTS}
+    listed = {"qmm.h": sbb.EXPORTS, "qmm_probe.h": probe.EXPORTS, "gdn.h": gdn.EXPORTS}
     assert set(headers) <= set(listed), headers
     for hname in headers:
         names = declared_functions(hname)
