@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--ms", default="1,4,8,16")
     ap.add_argument("--extra-ms", default="32",
                     help="row counts also timed per pass but not part of value ('' for none)")
-    ap.add_argument("--mode", default="pass", choices=["pass", "configs", "kernels", "copy"])
+    ap.add_argument("--mode", default="pass", choices=["pass", "configs", "kernels", "copy", "gdn"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ids", action="store_true", help="skip the expert-indexed record")
@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-projection pass")
     ap.add_argument("--no-configs", action="store_true", help="skip the single-matrix workloads")
     ap.add_argument("--no-probes", action="store_true", help="skip the memory-system probes")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the recurrent-update record")
     ap.add_argument("--seq-out", default="", help="--mode kernels: write the launch sequence here")
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--layers", type=int, default=64, help="(for quick tests only; the metric needs 64)")
@@ -688,6 +689,103 @@ def int4_measure(torch, sbb, synth, acc, h, reps=5):
                         "seeded random codes, 144-byte groups", "shapes": out}
 
 
+GDN_LAYERS, GDN_B, GDN_H, GDN_M, GDN_L, GDN_D = 48, 32, 48, 4, 8, 128
+
+
+def gdn_flops(n_log, M, H, D=GDN_D):
+    """Algorithmic flops of a recurrent-update call: per state element and row,
+    s . k (2), the decay and write alpha s + u k (3), and s . q for a new row
+    (2); the per-row scalars are not counted."""
+    return int(sum(H * D * D * (5 * int(nl) + 7 * M) for nl in n_log))
+
+
+def gdn_measure(torch, reps=10):
+    """The Gated DeltaNet update with log replay (include/gdn.h) on the
+    verify pass's recurrent layers: 48 layers, each a call over 32 sequences
+    of 48 heads of 128 x 128 fp32 state (3 MiB per sequence and layer, 4.8 GB
+    for the 48 layers), 4 new rows per sequence and a log of n_log[b] = b mod 9
+    kept rows, all folded into the base state (commit = n_log). A pass is the
+    48 calls back to back, replayed as a graph; kernel durations come from
+    events around eager single calls."""
+    import numpy as np
+    import synth
+    from skinny_bit_block_amd import gdn
+    B, H, M, L, D = GDN_B, GDN_H, GDN_M, GDN_L, GDN_D
+    dev = torch.device("cuda:0")
+    base = torch.from_numpy(synth.gdn_state(B, H, D, D, tensor=700, seed=SEED)).to(dev)
+    states = [base] + [base.clone() for _ in range(GDN_LAYERS - 1)]
+    log = {k: torch.from_numpy(v).to(dev) for k, v in
+           synth.gdn_rows(B, L, H, D, D, tensor=701, seed=SEED, queries=False).items()}
+    new = {k: torch.from_numpy(v).to(dev) for k, v in synth.gdn_rows(B, M, H, D, D, tensor=702, seed=SEED).items()}
+    n_log_h = np.array([b % 9 for b in range(B)], dtype=np.int32)
+    n_log = torch.from_numpy(n_log_h).to(dev)
+    commit = n_log.clone()
+    o = torch.empty((B, M, H, D), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def go(sp):
+        for st in states:
+            gdn.gdn_replay_update(st, log, n_log, new, o, commit=commit, stream=sp)
+
+    go(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.graph(g, stream=side):
+        go(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    ts.sort()
+    t_pass = ts[len(ts) // 2]
+    # kernel durations: events around single eager calls (each call ~tens of us)
+    ks = []
+    for st in states[:16]:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gdn.gdn_replay_update(st, log, n_log, new, o, commit=commit, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ks.append(a.elapsed_time(b) * 1e-3)
+    ks.sort()
+    t_call = ks[len(ks) // 2]
+    nbytes = gdn.gdn_call_bytes(B, M, H, D, D, int(n_log_h.sum()), int((n_log_h > 0).sum()))
+    flops = gdn_flops(n_log_h, M, H)
+    hbm_s, alu_s = nbytes / 8e12, flops / 157.3e12
+    del states, base
+    torch.cuda.empty_cache()
+    per_call_pass = t_pass / GDN_LAYERS
+    return {
+        "workload": "Gated DeltaNet recurrent update with log replay: %d layers x %d sequences x %d "
+                    "heads of 128x128 fp32 state (3 MiB per sequence and layer), %d new rows, logs of "
+                    "b mod 9 kept rows folded into the base state; synthetic states and rows"
+                    % (GDN_LAYERS, B, H, M),
+        "ms_per_pass_48_layers": round(t_pass * 1e3, 4),
+        "us_per_call_in_pass": round(per_call_pass * 1e6, 3),
+        "kernel_us_per_call": round(t_call * 1e6, 3),
+        "bytes_per_call": nbytes, "flops_per_call": flops,
+        "gbs": round(nbytes / t_call / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t_call / 8e12, 2),
+        "gbs_in_pass": round(nbytes / per_call_pass / 1e9, 1),
+        "tflops": round(flops / t_call / 1e12, 2),
+        "roofline": {"bound": "hbm" if hbm_s >= alu_s else "alu",
+                     "achieved": round(nbytes / t_call / 1e9, 1) if hbm_s >= alu_s else round(flops / t_call / 1e12, 2),
+                     "peak": 8000.0 if hbm_s >= alu_s else 157.3,
+                     "unit": "GB/s" if hbm_s >= alu_s else "TFLOP/s",
+                     "frac": round((hbm_s if hbm_s >= alu_s else alu_s) / t_call, 4),
+                     "floor_us": round(max(hbm_s, alu_s) * 1e6, 3),
+                     "alu_floor_us_fp32_vector": round(alu_s * 1e6, 3)},
+    }
+
+
 def pass_record(P, per_m, acc, ceiling=None):
     out = {}
     for M, ms_ in per_m.items():
@@ -787,6 +885,10 @@ def mode_pass(args, torch, sbb, synth, acc):
     if not args.no_int4:
         log("plain INT4 product...")
         out["int4"] = int4_measure(torch, sbb, synth, acc, P.h)
+    if not args.no_gdn:
+        log("recurrent update with log replay...")
+        out["gdn"] = gdn_measure(torch)
+        log(json.dumps(out["gdn"]))
     value = acc.gbs(P.weight_bytes * len(ms), ms_step * 1e-3)
     prop = torch.cuda.get_device_properties(0)
     line = {
@@ -887,6 +989,9 @@ def main():
         sys.exit(1)
     if args.mode == "copy":
         return mode_copy(args, torch)
+    if args.mode == "gdn":  # the recurrent-update record alone (for profiler runs)
+        print(json.dumps(gdn_measure(torch, reps=max(1, args.steps))))
+        return
     import synth
     import skinny_bit_block_amd as sbb
     from skinny_bit_block_amd import accounting as acc

@@ -161,21 +161,20 @@ __device__ __forceinline__ int fold_point(const Walk& w, int r, int stop, float 
   return stop;
 }
 
-// One workgroup = one wave = 64 value rows of one head of one sequence:
-// blockIdx.x = (b * H + h) * 2 + half.
-__global__ void __launch_bounds__(64) gdn_replay_kernel(
+// One workgroup = one head of one sequence (blockIdx.x = b * H + h), its two
+// waves the two halves of the head's 128 value rows. The waves of a head read
+// the same keys, queries and gates; in one workgroup they share a compute
+// unit and so its scalar cache (consecutive workgroups go to different XCDs).
+__global__ void __launch_bounds__(64 * kWavesPerHead) gdn_replay_kernel(
     float* __restrict__ state, const float* __restrict__ k_log, const float* __restrict__ v_log,
     const float* __restrict__ g_log, const float* __restrict__ b_log,
     const int32_t* __restrict__ n_log, int L, const float* __restrict__ q,
     const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ commit, float* __restrict__ o,
     int M, int H) {
-  const int lane = (int)threadIdx.x;
-  const int wg = (int)blockIdx.x;
-  const int half = wg % kWavesPerHead;
-  const int bh = wg / kWavesPerHead;
+  const int bh = (int)blockIdx.x;
   const int h = bh % H, b = bh / H;
-  const int i = half * kWaveRows + lane;  // this lane's value row
+  const int i = (int)threadIdx.x;  // this lane's value row: wave i / 64 holds half i / 64
 
   // the head's state (a wave-uniform base) and this lane's 32-bit offset
   float* const head = state + (size_t)bh * kDk * kDv;
@@ -237,9 +236,8 @@ int gdn_replay_update(float* state, const float* k_log, const float* v_log,
   if (dk != kDk || dv != kDv) return QMM_ERR_SHAPE;
   if (L > 0 && (!k_log || !v_log || !gate_log || !beta_log || !n_log)) return QMM_ERR_INVALID_ARG;
   if (M > 0 && (!q || !k || !v || !gate || !beta || !o)) return QMM_ERR_INVALID_ARG;
-  if (B > INT32_MAX / H || B * H > INT32_MAX / kWavesPerHead || L > INT32_MAX || M > INT32_MAX)
-    return QMM_ERR_INVALID_ARG;
-  const int64_t wgs = B * H * kWavesPerHead;
+  if (B > INT32_MAX / H || L > INT32_MAX || M > INT32_MAX) return QMM_ERR_INVALID_ARG;
+  const int64_t wgs = B * H;
   const void* ptrs[] = {state, k_log, v_log, gate_log, beta_log, n_log, q, k, v, gate, beta, commit, o};
   for (const void* p : ptrs)
     if ((uintptr_t)p & 3) return QMM_ERR_ALIGN;
@@ -260,7 +258,7 @@ int gdn_replay_update(float* state, const float* k_log, const float* v_log,
     if (overlaps(state, sb, a.p, a.n) || overlaps(o, ob, a.p, a.n)) return QMM_ERR_OVERLAP;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return QMM_ERR_NO_DEVICE;
-  hipLaunchKernelGGL(gdn_replay_kernel, dim3((unsigned)wgs), dim3(kWaveRows), 0, stream, state,
+  hipLaunchKernelGGL(gdn_replay_kernel, dim3((unsigned)wgs), dim3(kDv), 0, stream, state,
                      k_log, v_log, gate_log, beta_log, L > 0 ? n_log : nullptr, (int)L, q, k, v,
                      gate, beta, commit, o, (int)M, (int)H);
   return hipGetLastError() == hipSuccess ? QMM_OK : QMM_ERR_HIP;
