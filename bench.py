@@ -467,6 +467,7 @@ def cpu_baseline(budget_s, seconds_single=2.0):
     shapes = [("square", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408),
               ("lm_head", 151936, 5120)]
     Ms = (1, 4, 8, 16)
+    cores = oracle.threads()  # the OpenMP team of the sampled calls
     share = budget_s / (len(shapes) * len(Ms))
     rates, rows_used = {}, {}
     total_s = 0.0
@@ -504,12 +505,12 @@ def cpu_baseline(budget_s, seconds_single=2.0):
         total_s += dt * n
         single["all_threads" if threads == 0 else "one_thread"] = {
             "ms_per_call": round(dt * 1e3, 3), "weight_gbs": round(acc.gbs(acc.weight_bytes(N, K), dt), 4)}
-    return {"value": round(value, 4), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": round(value, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": "fp64 oracle on rows of one seeded matrix of each pass shape (5120x5120, "
                       "34816x5120, 5120x17408, 151936x5120; up to 8192 rows) at M=1/4/8/16, "
                       "%.1f s of wall time on %d threads; value = weight GB/s of a whole pass "
                       "(513 calls' bytes at the sampled per-shape rates) over the four row counts"
-                      % (total_s, oracle.threads()),
+                      % (total_s, cores),
             "ms_per_pass": {str(M): round(pass_s[M] * 1e3, 1) for M in Ms},
             "per_shape_gbs": {"%s M=%d" % k: round(v / 1e9, 4) for k, v in sorted(rates.items())},
             "single_2048x2048_m4": single}

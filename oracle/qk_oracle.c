@@ -118,11 +118,12 @@ int oracle_qmm_rows(const float* x, const uint8_t* W, int64_t M, int64_t N, int6
   const int64_t nb = K / 256;
   int bad = 0;
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  /* a count for this call only (the process default stays as it was) */
+  const int team = nthreads > 0 ? nthreads : omp_get_max_threads();
 #else
   (void)nthreads;
 #endif
-#pragma omp parallel
+#pragma omp parallel num_threads(team)
   {
     double w[256];
     double* acc = (double*)malloc(sizeof(double) * 2 * (size_t)M);
