@@ -87,6 +87,11 @@ constexpr TableEntry kTable[] = {
     {5120, 17408, 17, QMM_KERNEL_TILED, 6, 12, 1},
     // single 2048 x 2048 projection (4 rows): every slice in one workgroup
     {2048, 2048, 4, QMM_KERNEL_TILED, 4, 4, 4},
+    // five same-input 5120-wide projections as one call (N = 5 x 5120)
+    {25600, 5120, 1, QMM_KERNEL_VECTOR, 8, 1, 1},
+    {25600, 5120, 2, QMM_KERNEL_TILED, 8, 1, 1},
+    {25600, 5120, 9, QMM_KERNEL_TILED, 8, 2, 1},
+    {25600, 5120, 17, QMM_KERNEL_TILED, 8, 4, 1},
     // lm_head
     {151936, 5120, 1, QMM_KERNEL_VECTOR, 8, 1, 1},
     {151936, 5120, 2, QMM_KERNEL_TILED, 8, 1, 1},
