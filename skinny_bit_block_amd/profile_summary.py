@@ -210,6 +210,52 @@ def counters(args):
         sys.stderr.write("counter guard failed on %d dispatches\n" % len(guard))
 
 
+def stats(args):
+    """One kernel's rocprofv3 figures: the --stats row of a kernel-trace run,
+    and, when counter runs are given, its calibrated FETCH_SIZE / WRITE_SIZE
+    bytes per dispatch against its algorithmic bytes."""
+    want = args.kernel
+    lines = ["# rocprofv3 summary: %s" % want, "", "commands (repository root, after cd /tmp && "
+             "export TMPDIR=/tmp):"]
+    lines += ["  " + c for c in args.command.split(" ;; ")]
+    if args.sha:
+        lines.append("kernel_source_sha256: %s" % args.sha)
+    lines.append("")
+    with open(args.stats) as f:
+        for row in csv.DictReader(f):
+            if want in row["Name"]:
+                lines += ["| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|",
+                          "| %s | %s | %.3f | %.3f | %.3f |" % (want, row["Calls"], float(row["AverageNs"]) * 1e-3,
+                                                            float(row["MinNs"]) * 1e-3, float(row["MaxNs"]) * 1e-3)]
+                avg_us = float(row["AverageNs"]) * 1e-3
+                break
+        else:
+            raise SystemExit("%s not in %s" % (want, args.stats))
+    lines.append("mean_kernel_us[%s]: %.3f" % (want, avg_us))
+    if args.fetch:
+        def per_dispatch(path, name):
+            vals = {}
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if want in _col(row, "Kernel_Name", "KernelName") and _col(row, "Counter_Name", "CounterName") == name:
+                        did = int(_col(row, "Dispatch_Id", "Dispatch_ID", "DispatchId"))
+                        vals[did] = vals.get(did, 0.0) + float(_col(row, "Counter_Value", "CounterValue"))
+            return list(vals.values())
+        ff = (1 << 30) / 1024.0 / _copy_kib(args.copy_fetch, "FETCH_SIZE")
+        wf = (1 << 30) / 1024.0 / _copy_kib(args.copy_write, "WRITE_SIZE")
+        fv, wv = per_dispatch(args.fetch, "FETCH_SIZE"), per_dispatch(args.write, "WRITE_SIZE")
+        fb = sum(fv) / len(fv) * 1024.0 * ff
+        wb = sum(wv) / len(wv) * 1024.0 * wf
+        lines += ["", "calibration (plain 1 GiB device copy): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (ff, wf),
+                  "dispatches: %d (fetch run), %d (write run)" % (len(fv), len(wv)),
+                  "fetch bytes per dispatch: %.0f" % fb, "write bytes per dispatch: %.0f" % wb]
+        if args.algorithmic:
+            lines.append("algorithmic bytes per dispatch: %d (ratio %.3f)"
+                         % (args.algorithmic, (fb + wb) / args.algorithmic))
+        lines.append("traffic_bytes_per_dispatch[%s]: %.0f" % (want, fb + wb))
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -222,8 +268,17 @@ def main(argv=None):
     c = sub.add_parser("counters")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--seq", "--command", "--out"):
         c.add_argument(a, required=True)
+    st = sub.add_parser("stats")
+    st.add_argument("--kernel", required=True)
+    st.add_argument("--stats", required=True)
+    st.add_argument("--command", required=True)
+    st.add_argument("--out", required=True)
+    st.add_argument("--sha", default="")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
+        st.add_argument(a, default="")
+    st.add_argument("--algorithmic", type=int, default=0)
     args = ap.parse_args(argv)
-    {"trace": trace, "counters": counters}[args.what](args)
+    {"trace": trace, "counters": counters, "stats": stats}[args.what](args)
 
 
 if __name__ == "__main__":
