@@ -145,3 +145,37 @@ def test_layer_of_32_sequences():
     sub = lambda d: None if d is None else {k: v[pick_b][:, :, pick_h] for k, v in d.items()}
     check(state[pick_b][:, pick_h], sub(log), [n_log[b] for b in pick_b], sub(new),
           [commit[b] for b in pick_b], st[pick_b][:, pick_h], o[pick_b][:, :, pick_h], "32 x 48")
+
+
+def test_graph_replays_match_eager_calls():
+    # a captured call replayed several times (with eager work and syncs in
+    # between) against the same calls made eagerly on a second copy of the
+    # state: committing calls change the state each time, so every replay's
+    # outputs and state must equal the matching eager call's, bitwise
+    B, H, L, M = 3, 4, 4, 3
+    state, log, new = make(B, H, L, M, tensor=700)
+    n_log = torch.tensor([4, 1, 3], dtype=torch.int32, device="cuda")
+    commit = torch.tensor([5, 0, 6], dtype=torch.int32, device="cuda")
+    lg, nw = dev(log), dev(new)
+    st_g = torch.from_numpy(state.copy()).cuda()
+    st_e = torch.from_numpy(state.copy()).cuda()
+    o_g = torch.zeros((B, M, H, D), device="cuda")
+    o_e = torch.zeros((B, M, H, D), device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        gdn.gdn_replay_update(st_g, lg, n_log, nw, o_g, commit=commit, stream=side)
+    torch.cuda.synchronize()
+    # capture does not run the call: both copies are still the base state
+    assert torch.equal(st_g, st_e)
+    for step in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        gdn.gdn_replay_update(st_e, lg, n_log, nw, o_e, commit=commit)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), step
+        assert torch.equal(st_g, st_e), step
+        st_e.add_(0.0)  # eager work between replays
+    assert not torch.equal(st_g.cpu(), torch.from_numpy(state))  # the commits moved it
