@@ -84,6 +84,9 @@ def check(state, log, n_log, new, commit, st_gpu, o_gpu, what):
     (2, 2, 4, 0, [4, 2], [4, 1]),             # replay and commit only, no outputs
     (2, 2, 3, 2, [3, 1], None),               # no commit: states unchanged
     (4, 48, 8, 4, [0, 3, 8, 5], [0, 7, 12, 5]),  # a layer's 48 heads
+    (2, 2, 64, 8, [64, 33], [50, 72]),        # long logs (72-row walks)
+    (1, 1, 1, 1, [1], [2]),                   # one head, one kept row, one new row
+    (5, 1, 2, 1, [0, 1, 2, 0, 2], [1, 0, 3, 0, 1]),  # single-row walks, ragged
 ])
 def test_parity(B, H, L, M, n_log, commit):
     state, log, new = make(B, H, L, M, tensor=100 + B * 7 + H + L + M)
