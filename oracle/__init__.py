@@ -26,6 +26,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qk_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of qk_oracle.c to load instead (the
+# sanitizer build of the tests)
+_LOAD = os.environ.get("ORACLE_LIBRARY") or _LIB
 
 
 def build():
@@ -42,9 +45,9 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _LOAD == _LIB and not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(_LOAD)
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_scale_min.argtypes = [ctypes.c_void_p, ctypes.c_int,

@@ -12,7 +12,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqmm.so")
+# QMM_LIBRARY names another build of the same sources to load instead (the
+# host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("QMM_LIBRARY") or os.path.join(HERE, "libqmm.so")
 
 QMM_OK = 0
 QMM_ERR_INVALID_ARG = -1
