@@ -13,6 +13,9 @@ each one can be named by its shape and row count:
   counters: python -m skinny_bit_block_amd.profile_summary counters --fetch <csv> --write <csv>
                 --copy-fetch <csv> --copy-write <csv> --seq SEQ --command "..."
                 --out profiles/counters_pass_and_configs.txt
+  pipeline: python -m skinny_bit_block_amd.profile_summary pipeline --csv <csv> --seq SEQ
+                [--csv <csv> --seq SEQ ...] --command "..."
+                --out profiles/pipeline_counters_pass_and_configs.md
 
 Counter bytes are calibrated against a plain device copy of known size (bench.py
 --mode copy, 1 GiB): FETCH_SIZE and WRITE_SIZE are scaled so that the copy
@@ -256,6 +259,100 @@ def stats(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+# Pipeline counters of the library's kernels (rocprofv3 --pmc, raw SQ counters
+# in passes within the hardware's per-pass limits). A tile-block is one
+# 16-row tile times one 256-weight super-block: a wave's unit of work, so the
+# per-tile-block figures compare launch shapes and row counts directly.
+PIPELINE = [
+    # (label, how it is formed from the counters of one dispatch)
+    ("waves", lambda c, tb: c["SQ_WAVES"]),
+    ("mean waves resident per SIMD", lambda c, tb: c["SQ_WAVE_CYCLES"] / c["SQ_BUSY_CU_CYCLES"]),
+    ("share of wave time waiting to issue", lambda c, tb: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("VALU active share of busy SIMD time",
+     lambda c, tb: c["SQ_ACTIVE_INST_VALU"] / c["SQ_BUSY_CU_CYCLES"]),
+    ("VALU instructions per tile-block", lambda c, tb: c["SQ_INSTS_VALU"] / tb),
+    ("MFMA instructions per tile-block", lambda c, tb: c["SQ_INSTS_MFMA"] / tb),
+    ("MFMA busy cycles per tile-block", lambda c, tb: c["SQ_VALU_MFMA_BUSY_CYCLES"] / tb),
+    ("LDS instructions per tile-block", lambda c, tb: c["SQ_INSTS_LDS"] / tb),
+    ("LDS bank-conflict cycles per LDS instruction",
+     lambda c, tb: c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_INSTS_LDS"], 1.0)),
+    ("LDS active share of busy CU time",
+     lambda c, tb: c["SQ_ACTIVE_INST_LDS"] / c["SQ_BUSY_CU_CYCLES"]),
+]
+
+
+def _all_counters(path):
+    """{dispatch id: {counter: value summed over its dimensions}} of the library's kernels."""
+    vals = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if not _symbol(_col(row, "Kernel_Name", "KernelName")):
+                continue
+            did = int(_col(row, "Dispatch_Id", "Dispatch_ID", "DispatchId"))
+            name = _col(row, "Counter_Name", "CounterName")
+            d = vals.setdefault(did, {})
+            d[name] = d.get(name, 0.0) + float(_col(row, "Counter_Value", "CounterValue"))
+    return vals
+
+
+def tile_blocks(N, K):
+    return (N + 15) // 16 * (K // acc.BLOCK_WEIGHTS)
+
+
+def pipeline(args):
+    if len(args.csv) != len(args.seq):
+        raise SystemExit("one --seq per --csv")
+    by = {}
+    sha = None
+    for path, seqp in zip(args.csv, args.seq):
+        seq = json.load(open(seqp))
+        sha = seq["kernel_source_sha256"]
+        vals = _all_counters(path)
+        seen, disp = set(), []
+        for did, sym, row in _dispatches(path):
+            if did not in seen:
+                seen.add(did)
+                disp.append((did, sym, row))
+        for (did, sym, _), s in _align(disp, seq["launches"]):
+            for k in ((_key(s),) if _config(s) else (sym, _key(s))):
+                d = by.setdefault(k, {"n": {}, "c": {}, "tb": 0.0, "ntb": 0})
+                for name, v in vals[did].items():
+                    d["c"][name] = d["c"].get(name, 0.0) + v
+                    d["n"][name] = d["n"].get(name, 0) + 1
+                if path == args.csv[0]:
+                    d["tb"] += tile_blocks(s["N"], s["K"])
+                    d["ntb"] += 1
+    lines = ["# Pipeline counters per dispatch (rocprofv3 --pmc, raw SQ counters)", "",
+             "workload: bench.py --mode kernels (one eager pass at each M, two calls of each "
+             "single-matrix workload per M)",
+             "kernel_source_sha256: %s" % sha,
+             "commands (repository root, after cd /tmp && export TMPDIR=/tmp):"]
+    lines += ["  " + c for c in args.command.split(" ;; ")]
+    lines += ["", "Per dispatch means; a tile-block is one 16-row tile x one 256-weight super-block",
+              "(ceil(N/16) K/256 per matrix). Ratios: resident waves = SQ_WAVE_CYCLES /",
+              "SQ_BUSY_CU_CYCLES, which reads 1.0 for launch shapes with one 4-wave workgroup per",
+              "busy CU, i.e. waves per SIMD; waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; VALU active",
+              "= SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES; LDS active = SQ_ACTIVE_INST_LDS /",
+              "SQ_BUSY_CU_CYCLES; bank-conflict cycles per LDS instruction = SQ_LDS_BANK_CONFLICT /",
+              "SQ_INSTS_LDS. (kernel keys: the full-pass launches; \"config\" keys: the single-matrix",
+              "workloads)", ""]
+    labels = [l for l, _ in PIPELINE]
+    lines.append("| key | dispatches | " + " | ".join(labels) + " |")
+    lines.append("|---|---|" + "---|" * len(labels))
+    for k, d in sorted(by.items()):
+        c = {name: v / d["n"][name] for name, v in d["c"].items()}
+        tb = d["tb"] / max(d["ntb"], 1)
+        cells = []
+        for _, f in PIPELINE:
+            try:
+                v = f(c, tb)
+                cells.append("%.0f" % v if abs(v) >= 100 else "%.3g" % v)
+            except (KeyError, ZeroDivisionError):
+                cells.append("-")
+        lines.append("| %s | %d | %s |" % (k, d["ntb"], " | ".join(cells)))
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -277,8 +374,13 @@ def main(argv=None):
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
         st.add_argument(a, default="")
     st.add_argument("--algorithmic", type=int, default=0)
+    pp = sub.add_parser("pipeline")
+    pp.add_argument("--csv", action="append", required=True, help="a counter_collection.csv (repeat)")
+    pp.add_argument("--seq", action="append", required=True, help="its launch sequence (repeat)")
+    pp.add_argument("--command", required=True)
+    pp.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    {"trace": trace, "counters": counters, "stats": stats}[args.what](args)
+    {"trace": trace, "counters": counters, "stats": stats, "pipeline": pipeline}[args.what](args)
 
 
 if __name__ == "__main__":

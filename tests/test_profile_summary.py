@@ -125,3 +125,59 @@ def test_committed_counters_pass_the_guard():
         acc.check_counter_bytes(float(val), acc.weight_bytes(N, K), what=key)
         checked += 1
     assert checked >= 20
+
+
+def _write_pipeline(path, seq, counters):
+    # counters: {name: f(launch) -> value per dispatch}; each value split over
+    # two dimension rows (summed by the tool), foreign dispatches in between
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        did = 3
+        for s in seq["launches"]:
+            for name in counters:
+                w.writerow([did - 1, "void qmm::zero_u32(unsigned int*, int)", name, 5.0])
+            for name, fn in counters.items():
+                v = fn(s)
+                w.writerow([did, "void qmm::%s(qmm::Args)" % s["symbol"], name, v / 2])
+                w.writerow([did, "void qmm::%s(qmm::Args)" % s["symbol"], name, v / 2])
+            did += 2
+
+
+def test_pipeline_summary(tmp_path):
+    seq = _seq()
+    json.dump(seq, open(tmp_path / "seq.json", "w"))
+    tb = lambda s: ps.tile_blocks(s["N"], s["K"])
+    # pass A: 110 VALU and 10 MFMA per tile-block, 6 waves resident, 40% waiting, VALU
+    # active 2000 against 1000 busy cycles (synthetic values: the tool only divides)
+    a = {"SQ_WAVES": lambda s: 1024.0, "SQ_WAVE_CYCLES": lambda s: 6000.0,
+         "SQ_BUSY_CU_CYCLES": lambda s: 1000.0, "SQ_WAIT_INST_ANY": lambda s: 2400.0,
+         "SQ_ACTIVE_INST_VALU": lambda s: 2000.0,
+         "SQ_INSTS_VALU": lambda s: 110.0 * tb(s), "SQ_INSTS_MFMA": lambda s: 10.0 * tb(s),
+         "SQ_VALU_MFMA_BUSY_CYCLES": lambda s: 64.0 * tb(s)}
+    # pass B: 12 LDS instructions per tile-block, 0.5 conflict cycles each
+    b = {"SQ_INSTS_LDS": lambda s: 12.0 * tb(s), "SQ_LDS_BANK_CONFLICT": lambda s: 6.0 * tb(s),
+         "SQ_ACTIVE_INST_LDS": lambda s: 300.0, "SQ_BUSY_CU_CYCLES": lambda s: 1000.0}
+    _write_pipeline(tmp_path / "a.csv", seq, a)
+    _write_pipeline(tmp_path / "b.csv", seq, b)
+    ps.main(["pipeline", "--csv", str(tmp_path / "a.csv"), "--seq", str(tmp_path / "seq.json"),
+             "--csv", str(tmp_path / "b.csv"), "--seq", str(tmp_path / "seq.json"),
+             "--command", "cmd a ;; cmd b", "--out", str(tmp_path / "p.md")])
+    text = open(tmp_path / "p.md").read()
+    assert "kernel_source_sha256: 0123456789abcdef" in text and "  cmd b" in text
+    cells = lambda l: [c.strip() for c in l.strip().strip("|").split("|")]
+    rows = {cells(l)[0]: cells(l) for l in text.splitlines() if l.startswith("| ")}
+    # columns: key, dispatches, waves, resident, waiting, VALU active, VALU/tb, MFMA/tb,
+    # MFMA busy/tb, LDS/tb, conflicts per LDS instruction, LDS active
+    r = rows["square M=1"]
+    assert r[1] == "2"
+    assert [float(x) for x in r[3:12]] == pytest.approx([6.0, 0.4, 2.0, 110, 10, 64, 12, 0.5, 0.3])
+    assert rows["qmm_tiled_kernel<1, false, 0>"][1] == "5"
+    assert rows["config single_2048 M=4"][1] == "1"
+    # a counter missing from every run leaves its column empty
+    (tmp_path / "c.csv").write_text(open(tmp_path / "a.csv").read().replace("SQ_INSTS_MFMA", "SQ_OTHER"))
+    ps.main(["pipeline", "--csv", str(tmp_path / "c.csv"), "--seq", str(tmp_path / "seq.json"),
+             "--command", "c", "--out", str(tmp_path / "q.md")])
+    r = [cells(l) for l in open(tmp_path / "q.md").read().splitlines() if l.startswith("| square M=1")][0]
+    assert r[7] == "-"
