@@ -17,7 +17,10 @@
 // puts a wave's 64 value rows of one key index in one contiguous 256-byte run,
 // so every state load and store is coalesced. Small per-lane state leaves
 // room for many waves per SIMD, which is what hides the latency of the row
-// loop (the scalar loads of each row's vectors, the exchange).
+// loop (the scalar loads of each row's vectors, the exchange). The state and
+// the outputs are each touched once per call, so their loads and stores are
+// non-temporal (they do not displace the rows' inputs, which every wave of a
+// head reads, from the caches).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -151,7 +154,7 @@ __device__ __forceinline__ void walk_rows(const Walk& w, Exchange& x, int quarte
                                           size_t& out_row, int r0, int r1) {
   for (int r = r0; r < r1; ++r) {
     const float2 t = exchange(x, w, quarter, part);
-    if (out_row != ~(size_t)0 && quarter == 0) w.o[out_row * kDv + w.i] = t.y;
+    if (out_row != ~(size_t)0 && quarter == 0) __builtin_nontemporal_store(t.y, w.o + out_row * kDv + w.i);
     out_row = OUT ? cur.row : ~(size_t)0;
     const float u = cur.beta * (cur.vi - cur.alpha * t.x);  // t.x = s . k_r
     const float Pn = next_scale(P, cur.alpha);
@@ -222,7 +225,7 @@ __global__ void __launch_bounds__(kThreads) gdn_replay_kernel(
   float* const head = state + (size_t)bh * kDk * kDv;
   float z[kKq];
 #pragma unroll
-  for (int e = 0; e < kKq; ++e) z[e] = head[(e0 + e) * kDv + i];
+  for (int e = 0; e < kKq; ++e) z[e] = __builtin_nontemporal_load(head + (e0 + e) * kDv + i);
   float P = 1.f;
 
   int nl = n_log ? n_log[b] : 0;
@@ -256,13 +259,13 @@ __global__ void __launch_bounds__(kThreads) gdn_replay_kernel(
       int li = i;
       asm("" : "+v"(li));
 #pragma unroll
-      for (int e = 0; e < kKq; ++e) head[(e0 + e) * kDv + li] = P * z[e];
+      for (int e = 0; e < kKq; ++e) __builtin_nontemporal_store(P * z[e], head + (e0 + e) * kDv + li);
     }
   }
   // the last new row's output
   if (out_row != ~(size_t)0) {
     const float2 t = exchange(x, w, quarter, part);
-    if (quarter == 0) o[out_row * kDv + i] = t.y;
+    if (quarter == 0) __builtin_nontemporal_store(t.y, o + out_row * kDv + i);
   }
 }
 
