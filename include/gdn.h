@@ -69,7 +69,8 @@ extern "C" {
  * n_log when L = 0, the new-row arrays and o when M = 0, and commit. All
  * arrays 4-byte aligned. The state must not overlap any other array and o
  * must not overlap the inputs. Returns QMM_OK, or QMM_ERR_INVALID_ARG (null
- * pointer, negative sizes, more than 2^31 - 1 workgroups), QMM_ERR_SHAPE (dk
+ * pointer, negative sizes, more than 2^31 - 1 workgroups, more than 2^40 log
+ * rows B L H or new rows B M H), QMM_ERR_SHAPE (dk
  * or dv not 128), QMM_ERR_ALIGN, QMM_ERR_OVERLAP, QMM_ERR_NO_DEVICE (no
  * current HIP device), QMM_ERR_HIP (launch failure); on an error nothing is
  * launched. */

@@ -290,6 +290,9 @@ int gdn_replay_update(float* state, const float* k_log, const float* v_log,
   if (L > 0 && (!k_log || !v_log || !gate_log || !beta_log || !n_log)) return QMM_ERR_INVALID_ARG;
   if (M > 0 && (!q || !k || !v || !gate || !beta || !o)) return QMM_ERR_INVALID_ARG;
   if (B > INT32_MAX / H || L > INT32_MAX || M > INT32_MAX) return QMM_ERR_INVALID_ARG;
+  // at most 2^40 rows of either kind, so that every byte count below is exact
+  if ((uint64_t)(B * H) * (uint64_t)L > (1ull << 40) || (uint64_t)(B * H) * (uint64_t)M > (1ull << 40))
+    return QMM_ERR_INVALID_ARG;
   const int64_t wgs = B * H;
   const void* ptrs[] = {state, k_log, v_log, gate_log, beta_log, n_log, q, k, v, gate, beta, commit, o};
   for (const void* p : ptrs)

@@ -54,6 +54,9 @@ def test_valid_arguments_reach_the_device_query():
     (dict(q=None), sbb.QMM_ERR_INVALID_ARG),
     (dict(o=None), sbb.QMM_ERR_INVALID_ARG),
     (dict(B=1 << 30, H=8), sbb.QMM_ERR_INVALID_ARG),  # more than 2^31 - 1 workgroups
+    (dict(B=1 << 20, H=16, L=(1 << 20) + 1), sbb.QMM_ERR_INVALID_ARG),  # over 2^40 log rows
+    (dict(B=1 << 20, H=16, M=(1 << 20) + 1), sbb.QMM_ERR_INVALID_ARG),  # over 2^40 new rows
+    (dict(B=(1 << 30) - 1, H=2, L=(1 << 31) - 1), sbb.QMM_ERR_INVALID_ARG),  # byte counts past 2^64
     (dict(state=STATE + 2), sbb.QMM_ERR_ALIGN),
     (dict(gate=NEW + (3 << 20) + 1), sbb.QMM_ERR_ALIGN),
     (dict(o=STATE + 4096), sbb.QMM_ERR_OVERLAP),               # o inside the state
