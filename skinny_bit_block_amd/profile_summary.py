@@ -268,6 +268,7 @@ PIPELINE = [
     ("waves", lambda c, tb: c["SQ_WAVES"]),
     ("mean waves resident per SIMD", lambda c, tb: c["SQ_WAVE_CYCLES"] / c["SQ_BUSY_CU_CYCLES"]),
     ("share of wave time waiting to issue", lambda c, tb: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("share of wave time waiting on counters", lambda c, tb: c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]),
     ("VALU active share of busy SIMD time",
      lambda c, tb: c["SQ_ACTIVE_INST_VALU"] / c["SQ_BUSY_CU_CYCLES"]),
     ("VALU instructions per tile-block", lambda c, tb: c["SQ_INSTS_VALU"] / tb),
@@ -331,7 +332,8 @@ def pipeline(args):
     lines += ["", "Per dispatch means; a tile-block is one 16-row tile x one 256-weight super-block",
               "(ceil(N/16) K/256 per matrix). Ratios: resident waves = SQ_WAVE_CYCLES /",
               "SQ_BUSY_CU_CYCLES, which reads 1.0 for launch shapes with one 4-wave workgroup per",
-              "busy CU, i.e. waves per SIMD; waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; VALU active",
+              "busy CU, i.e. waves per SIMD; waiting to issue = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES;",
+              "waiting on counters (s_waitcnt: memory, LDS) = SQ_WAIT_ANY / SQ_WAVE_CYCLES; VALU active",
               "= SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES; LDS active = SQ_ACTIVE_INST_LDS /",
               "SQ_BUSY_CU_CYCLES; bank-conflict cycles per LDS instruction = SQ_LDS_BANK_CONFLICT /",
               "SQ_INSTS_LDS. (kernel keys: the full-pass launches; \"config\" keys: the single-matrix",
