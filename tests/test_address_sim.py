@@ -324,6 +324,25 @@ def test_seeded_sweep_of_ragged_shapes(planner):
         n += 1
 
 
+# (N, K, row counts): x of the longest rows stays under 0.5 GB
+LONG_K = [(1, 1 << 24, (1, 7)), (17, 1 << 22, (1, 7)), (20, 1 << 20, (1, 7, 32)),
+          (5, 1 << 19, (1, 7, 32)), (33, 1 << 18, (1, 7, 32))]
+
+
+def test_long_k_plans(planner):
+    # K far beyond the workloads' (up to the largest the library takes, 2^24):
+    # many K slices over few row tiles, long 32-bit in-wave offsets; both
+    # kernels, at the row counts the GPU test runs
+    for N, K, Ms in LONG_K:
+        for M, kernel in ((1, sbb.KERNEL_AUTO), (1, sbb.KERNEL_TILED), (7, sbb.KERNEL_AUTO),
+                          (7, sbb.KERNEL_VECTOR), (32, sbb.KERNEL_AUTO)):
+            if M not in Ms:
+                continue
+            p = plan(planner, sbb.FORMAT_KQUANT, 0, M, N, K, kernel)
+            assert p is not None, (M, N, K, kernel)
+            replay(p, M, N, K, grids=(1,))
+
+
 def test_replay_catches_a_stage_past_the_slice_end():
     # the replay flags the fault class it guards: a partial stage whose clamp
     # starts from a stage wholly past the slice end wraps the 32-bit offset

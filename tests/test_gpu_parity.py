@@ -113,6 +113,25 @@ def test_small_tiled(h, M, N, K):
     check(y, yref, aref, "tiled M=%d N=%d K=%d" % (M, N, K))
 
 
+# K far beyond the workloads', up to the largest the library takes (2^24):
+# thousands of K slices over one to three row tiles (the same cases the host
+# address replay walks)
+LONG_K = [(1, 1 << 24, 1, sbb.KERNEL_AUTO), (1, 1 << 24, 1, sbb.KERNEL_TILED),
+          (1, 1 << 24, 7, sbb.KERNEL_AUTO), (1, 1 << 24, 7, sbb.KERNEL_VECTOR),
+          (17, 1 << 22, 1, sbb.KERNEL_AUTO), (17, 1 << 22, 7, sbb.KERNEL_VECTOR),
+          (20, 1 << 20, 7, sbb.KERNEL_AUTO), (20, 1 << 20, 32, sbb.KERNEL_AUTO),
+          (5, 1 << 19, 32, sbb.KERNEL_AUTO), (33, 1 << 18, 1, sbb.KERNEL_TILED),
+          (33, 1 << 18, 32, sbb.KERNEL_AUTO)]
+
+
+@pytest.mark.parametrize("N,K,M,kernel", LONG_K)
+def test_long_k(h, N, K, M, kernel):
+    x, W = inputs(M, N, K, tag=N + M + kernel + (K >> 18))
+    y = run(h, x, W, N, K, kernel=kernel)
+    yref, aref = oracle.qmm(x, W, N, K)
+    check(y, yref, aref, "long K: M=%d N=%d K=%d kernel %d" % (M, N, K, kernel))
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 0), (2, 3, 0), (4, 2, 0), (8, 5, 0), (8, 1, 0), (1, 10, 0),
                                    (4, 7, 500), (8, 4, 63),
                                    # fewer workgroups than tiles: waves walk several tiles
