@@ -343,6 +343,18 @@ def test_long_k_plans(planner):
             replay(p, M, N, K, grids=(1,))
 
 
+# the other weight formats' long-K GPU cases (M, N, K)
+LONG_K_FORMATS = [(1, 1, 1 << 22), (7, 5, 1 << 20), (32, 3, 1 << 18)]
+
+
+@pytest.mark.parametrize("fmt", [sbb.FORMAT_NVFP4, sbb.FORMAT_INT4])
+def test_long_k_plans_of_the_group_formats(planner, fmt):
+    for M, N, K in LONG_K_FORMATS:
+        p = plan(planner, fmt, 0, M, N, K)
+        assert p is not None, (fmt, M, N, K)
+        replay(p, M, N, K, grids=(1,))
+
+
 def test_replay_catches_a_stage_past_the_slice_end():
     # the replay flags the fault class it guards: a partial stage whose clamp
     # starts from a stage wholly past the slice end wraps the 32-bit offset

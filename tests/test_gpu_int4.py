@@ -74,6 +74,14 @@ def test_parity(h, M, N, K):
     check(run(h, x, groups, N, K), yref, aref, "M=%d N=%d K=%d" % (M, N, K))
 
 
+# K far beyond the workloads' (thousands of K slices over few row tiles); the
+# host address replay walks the same plans
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1 << 22), (7, 5, 1 << 20), (32, 3, 1 << 18)])
+def test_long_k(h, M, N, K):
+    x, _, _, groups, yref, aref = case(M, N, K, tensor=700 + M)
+    check(run(h, x, groups, N, K), yref, aref, "long K: M=%d N=%d K=%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("shape,wsplit", [((4, 1, 0), 1), ((8, 2, 0), 1), ((4, 5, 1), 1),
                                           ((4, 2, 0), 2), ((8, 10, 3), 2), ((2, 3, 1), 1),
                                           ((6, 2, 0), 2), ((3, 1, 0), 1)])
