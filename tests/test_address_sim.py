@@ -355,6 +355,17 @@ def test_long_k_plans_of_the_group_formats(planner, fmt):
         replay(p, M, N, K, grids=(1,))
 
 
+def test_long_k_expert_plans(planner):
+    # the expert-indexed long-K GPU cases: each slot streams one expert with
+    # the rows that use it
+    for M, E, N, K in [(7, 4, 5, 1 << 20), (32, 3, 3, 1 << 18), (2, 2, 17, 1 << 19)]:
+        for slots in sorted({1, min(M, E)}):
+            p = plan(planner, sbb.FORMAT_KQUANT, slots, M, N, K)
+            assert p is not None, (M, E, N, K, slots)
+            for m in sorted({1, M}):
+                replay(p, m, N, K, grids=(1,))
+
+
 def test_replay_catches_a_stage_past_the_slice_end():
     # the replay flags the fault class it guards: a partial stage whose clamp
     # starts from a stage wholly past the slice end wraps the 32-bit offset

@@ -79,6 +79,18 @@ def test_ids_parity(h, M, E, kind):
     check_ids(y, x, W, ids, E, N, K, "M=%d E=%d %s" % (M, E, kind))
 
 
+@pytest.mark.parametrize("M,E,N,K", [(7, 4, 5, 1 << 20), (32, 3, 3, 1 << 18), (2, 2, 17, 1 << 19)])
+def test_ids_long_k(h, M, E, N, K):
+    # K far beyond the workloads' (thousands of K slices per expert slot); the
+    # host address replay walks the same plans
+    rng = np.random.default_rng(M + E)
+    ids = rng.integers(0, E, M)
+    W = experts(E, N, K, 870 + E)
+    x = synth.acts(M, K, tensor=880 + M)
+    y = run_ids(h, x, W, ids, E, N, K)
+    check_ids(y, x, W, ids, E, N, K, "long K: M=%d E=%d N=%d K=%d" % (M, E, N, K))
+
+
 @pytest.mark.parametrize("shape,wsplit", [((4, 3, 0), 0), ((4, 2, 2), 2), ((2, 1, 1), 0),
                                           ((8, 5, 0), 0), ((4, 4, 0), 4)])
 def test_ids_launch_shapes(h, shape, wsplit):
