@@ -16,6 +16,9 @@ each one can be named by its shape and row count:
   pipeline: python -m skinny_bit_block_amd.profile_summary pipeline --csv <csv> --seq SEQ
                 [--csv <csv> --seq SEQ ...] --command "..."
                 --out profiles/pipeline_counters_pass_and_configs.md
+  kernel-counters: python -m skinny_bit_block_amd.profile_summary kernel-counters
+                --csv <csv> [--csv <csv> ...] --kernel NAME --command "..." --out FILE
+                (one kernel's counters averaged over its dispatches, any workload)
 
 Counter bytes are calibrated against a plain device copy of known size (bench.py
 --mode copy, 1 GiB): FETCH_SIZE and WRITE_SIZE are scaled so that the copy
@@ -355,6 +358,52 @@ def pipeline(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def kernel_counters(args):
+    """Pipeline counters of one kernel (any symbol containing --kernel), averaged
+    over its dispatches in one or more counter runs, with the same ratios as
+    the pipeline summary (per wave instead of per tile-block)."""
+    per = {}
+    for path in args.csv:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if args.kernel not in _col(row, "Kernel_Name", "KernelName"):
+                    continue
+                key = (path, int(_col(row, "Dispatch_Id", "Dispatch_ID", "DispatchId")))
+                d = per.setdefault(key, {})
+                name = _col(row, "Counter_Name", "CounterName")
+                d[name] = d.get(name, 0.0) + float(_col(row, "Counter_Value", "CounterValue"))
+    if not per:
+        raise SystemExit("no dispatch of %s" % args.kernel)
+    tot, cnt = {}, {}
+    for d in per.values():
+        for k, v in d.items():
+            tot[k] = tot.get(k, 0.0) + v
+            cnt[k] = cnt.get(k, 0) + 1
+    c = {k: tot[k] / cnt[k] for k in tot}
+    lines = ["# Pipeline counters: %s" % args.kernel, "",
+             "commands (repository root, after cd /tmp && export TMPDIR=/tmp):"]
+    lines += ["  " + x for x in args.command.split(" ;; ")]
+    if args.sha:
+        lines.append("kernel_source_sha256: %s" % args.sha)
+    lines += ["", "dispatches: %d (means per dispatch; counters summed over their dimensions)"
+              % (len(per) // max(len(args.csv), 1)), ""]
+    for k in sorted(c):
+        lines.append("%s: %.6g" % (k, c[k]))
+    ratios = [
+        ("mean waves resident per SIMD", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES"),
+        ("share of wave time waiting on counters", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+        ("share of wave time waiting to issue", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+        ("VALU active share of busy SIMD time", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CU_CYCLES"),
+        ("LDS active share of busy CU time", "SQ_ACTIVE_INST_LDS", "SQ_BUSY_CU_CYCLES"),
+        ("VALU instructions per wave", "SQ_INSTS_VALU", "SQ_WAVES"),
+    ]
+    lines.append("")
+    for label, a, b in ratios:
+        if a in c and b in c and c[b]:
+            lines.append("%s: %.4g" % (label, c[a] / c[b]))
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -381,8 +430,15 @@ def main(argv=None):
     pp.add_argument("--seq", action="append", required=True, help="its launch sequence (repeat)")
     pp.add_argument("--command", required=True)
     pp.add_argument("--out", required=True)
+    kc = sub.add_parser("kernel-counters")
+    kc.add_argument("--csv", action="append", required=True, help="a counter_collection.csv (repeat)")
+    kc.add_argument("--kernel", required=True)
+    kc.add_argument("--command", required=True)
+    kc.add_argument("--out", required=True)
+    kc.add_argument("--sha", default="")
     args = ap.parse_args(argv)
-    {"trace": trace, "counters": counters, "stats": stats, "pipeline": pipeline}[args.what](args)
+    {"trace": trace, "counters": counters, "stats": stats, "pipeline": pipeline,
+     "kernel-counters": kernel_counters}[args.what](args)
 
 
 if __name__ == "__main__":

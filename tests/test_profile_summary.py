@@ -182,3 +182,26 @@ def test_pipeline_summary(tmp_path):
              "--command", "c", "--out", str(tmp_path / "q.md")])
     r = [cells(l) for l in open(tmp_path / "q.md").read().splitlines() if l.startswith("| square M=1")][0]
     assert r[8] == "-"
+
+
+def test_kernel_counters(tmp_path):
+    # one kernel's counters over its dispatches; other kernels are ignored
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(tmp_path / "k.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        for did in (1, 2):
+            for name, v in (("SQ_WAVES", 100.0), ("SQ_WAVE_CYCLES", 5000.0), ("SQ_BUSY_CU_CYCLES", 1000.0),
+                            ("SQ_WAIT_ANY", 2000.0 * did), ("SQ_INSTS_VALU", 3000.0)):
+                w.writerow([did, "gdn_replay_kernel(float*, ...)", name, v / 2])
+                w.writerow([did, "gdn_replay_kernel(float*, ...)", name, v / 2])
+            w.writerow([did + 10, "other_kernel", "SQ_WAVES", 7.0])
+    ps.main(["kernel-counters", "--csv", str(tmp_path / "k.csv"), "--kernel", "gdn_replay_kernel",
+             "--command", "c1 ;; c2", "--out", str(tmp_path / "k.md"), "--sha", "abc"])
+    text = open(tmp_path / "k.md").read()
+    assert "dispatches: 2" in text and "  c2" in text and "kernel_source_sha256: abc" in text
+    assert "SQ_WAVES: 100" in text
+    assert "mean waves resident per SIMD: 5" in text
+    assert "share of wave time waiting on counters: 0.6" in text  # mean of 2000, 4000 over 5000
+    assert "VALU instructions per wave: 30" in text
+    assert "VALU active share" not in text  # SQ_ACTIVE_INST_VALU not collected
