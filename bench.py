@@ -21,8 +21,10 @@ qmm_set_launch_events hook), which is what rocprofv3's kernel trace measures.
 Other modes: --mode configs (the single-matrix workloads only), --mode kernels
 (only the event-timed eager launches, for rocprofv3 runs; --seq-out writes
 the launch sequence that skinny_bit_block_amd/profile_summary.py maps the
-trace onto), --mode copy (a plain device copy of known size, the
-calibration of the FETCH_SIZE / WRITE_SIZE counters).
+trace onto), --mode switch (both kernels forced at 1..8 rows on every pass
+shape, for the rocprofv3 run behind the switch point), --mode copy (a plain
+device copy of known size, the calibration of the FETCH_SIZE / WRITE_SIZE
+counters).
 """
 import argparse
 import ctypes
@@ -64,7 +66,7 @@ def parse():
     ap.add_argument("--ms", default="1,4,8,16")
     ap.add_argument("--extra-ms", default="32",
                     help="row counts also timed per pass but not part of value ('' for none)")
-    ap.add_argument("--mode", default="pass", choices=["pass", "configs", "kernels", "copy", "gdn"])
+    ap.add_argument("--mode", default="pass", choices=["pass", "configs", "kernels", "switch", "copy", "gdn"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ids", action="store_true", help="skip the expert-indexed record")
@@ -75,7 +77,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the single-matrix workloads")
     ap.add_argument("--no-probes", action="store_true", help="skip the memory-system probes")
     ap.add_argument("--no-gdn", action="store_true", help="skip the recurrent-update record")
-    ap.add_argument("--seq-out", default="", help="--mode kernels: write the launch sequence here")
+    ap.add_argument("--seq-out", default="", help="--mode kernels / switch: write the launch sequence here")
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--layers", type=int, default=64, help="(for quick tests only; the metric needs 64)")
     return ap.parse_args()
@@ -976,6 +978,84 @@ def mode_kernels(args, torch, sbb, synth, acc):
                       for k, v in sorted(sym.items())}))
 
 
+SWITCH_SHAPES = [(5120, 5120), (34816, 5120), (5120, 17408), (151936, 5120)]
+
+
+def mode_switch(args, torch, sbb, synth, acc):
+    """Both kernels forced at 1..8 rows on every matrix shape of the pass, for
+    rocprofv3 runs that decide the row-vector (VALU dot2) / tiled (MFMA) switch
+    point. Each (shape, M, kernel) runs every launch shape the table holds for
+    the matrix (its entries from 1 to 16 rows) that fits at M rows, each three
+    times on a rotation of distinct copies of the matrix larger than the
+    last-level cache (cold weights). --seq-out writes the launch sequence."""
+    from skinny_bit_block_amd.events import EventPool
+    lib = sbb.load()
+    h = sbb.qmm_create(0)
+    stream = torch.cuda.current_stream()
+    pool = EventPool(1)
+    seq, res = [], {}
+    for N, K in SWITCH_SHAPES:
+        nb = acc.weight_bytes(N, K)
+        copies = max(3, -(-(512 << 20) // nb))
+        host = synth.weights(N, K, tensor=11, seed=SEED).reshape(-1)
+        W = torch.empty(copies * nb, dtype=torch.uint8, device="cuda")
+        for c in range(copies):
+            W[c * nb:(c + 1) * nb].copy_(torch.from_numpy(host))
+        rot = 0
+        for M in range(1, 9):
+            x = torch.from_numpy(synth.acts(M, K, tensor=12, seed=SEED)).cuda()
+            y = torch.empty((M, N), device="cuda")
+            for kernel in (sbb.KERNEL_VECTOR, sbb.KERNEL_TILED):
+                sbb.qmm_set_kernel(h, sbb.KERNEL_AUTO)
+                sbb.qmm_set_shape(h, 0, 0, 0)
+                sbb.qmm_set_wave_splits(h, 0)
+                table_kernel = sbb.KERNEL_NAMES[sbb.qmm_query_plan(h, M, N, K)["kernel"]]
+                shapes = []
+                for m_src in [M] + list(range(1, 17)):
+                    p = sbb.qmm_query_plan(h, m_src, N, K)
+                    s = (p["waves_per_wg"], p["splits"], p["wave_splits"])
+                    if s not in shapes:
+                        shapes.append(s)
+                for waves, splits, wsplit in shapes:
+                    sbb.qmm_set_kernel(h, kernel)
+                    sbb.qmm_set_shape(h, waves, splits, 0)
+                    sbb.qmm_set_wave_splits(h, wsplit)
+                    try:
+                        sbb.qmm_query_plan(h, M, N, K)
+                    except sbb.QmmError:
+                        continue  # that shape's staged x does not fit at M rows
+                    name = "qmm_vector_kernel<%d>" % M if kernel == sbb.KERNEL_VECTOR \
+                        else "qmm_tiled_kernel<1, false, 0>"
+                    times = []
+                    for _ in range(3):
+                        Wc = W[(rot % copies) * nb:(rot % copies + 1) * nb]
+                        rot += 1
+                        sbb.qmm_set_launch_events(h, *pool.pairs[0])
+                        rc = lib.qmm_run(h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(Wc.data_ptr()),
+                                         ctypes.c_void_p(y.data_ptr()), M, N, K,
+                                         ctypes.c_void_p(stream.cuda_stream))
+                        if rc:
+                            raise RuntimeError(sbb.qmm_status_string(rc))
+                        torch.cuda.synchronize()
+                        times.append(pool.elapsed_ms(0) * 1e3)
+                        seq.append({"symbol": name, "shape": shape_class(N, K), "M": M, "N": N, "K": K,
+                                    "kernel": sbb.KERNEL_NAMES[kernel], "table_kernel": table_kernel,
+                                    "launch": "%d/%d/%d" % (waves, splits, wsplit)})
+                    key = "%s M=%d %s %d/%d/%d" % (shape_class(N, K), M, sbb.KERNEL_NAMES[kernel],
+                                                   waves, splits, wsplit)
+                    res[key] = round(sum(times) / len(times), 3)
+            sbb.qmm_set_kernel(h, sbb.KERNEL_AUTO)
+            sbb.qmm_set_shape(h, 0, 0, 0)
+            sbb.qmm_set_wave_splits(h, 0)
+        del W
+        torch.cuda.empty_cache()
+    pool.close()
+    sbb.qmm_destroy(h)
+    if args.seq_out:
+        json.dump({"kernel_source_sha256": kernel_source_sha(), "launches": seq}, open(args.seq_out, "w"))
+    print(json.dumps({"event_us": res}))
+
+
 def mode_configs(args, torch, sbb, synth, acc):
     """The single-matrix workloads only."""
     h = sbb.qmm_create(0)
@@ -1018,7 +1098,8 @@ def main():
     import synth
     import skinny_bit_block_amd as sbb
     from skinny_bit_block_amd import accounting as acc
-    {"pass": mode_pass, "configs": mode_configs, "kernels": mode_kernels}[args.mode](
+    {"pass": mode_pass, "configs": mode_configs, "kernels": mode_kernels,
+     "switch": mode_switch}[args.mode](
         args, torch, sbb, synth, acc)
 
 

@@ -16,6 +16,9 @@ each one can be named by its shape and row count:
   pipeline: python -m skinny_bit_block_amd.profile_summary pipeline --csv <csv> --seq SEQ
                 [--csv <csv> --seq SEQ ...] --command "..."
                 --out profiles/pipeline_counters_pass_and_configs.md
+  switch:   python -m skinny_bit_block_amd.profile_summary switch --csv <kernel_trace.csv>
+                --seq SEQ --command "..." --out profiles/switch_point_vector_vs_tiled.md
+                (SEQ from bench.py --mode switch: both kernels forced at 1..8 rows)
   kernel-counters: python -m skinny_bit_block_amd.profile_summary kernel-counters
                 --csv <csv> [--csv <csv> ...] --kernel NAME --command "..." --out FILE
                 (one kernel's counters averaged over its dispatches, any workload)
@@ -404,6 +407,66 @@ def kernel_counters(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def switch(args):
+    """The row-vector (VALU dot2) / tiled (MFMA) comparison of bench.py --mode
+    switch: per (shape, M, kernel) the mean kernel duration of each launch shape
+    tried, the faster kernel with its best shape, and the row count from which
+    the tiled kernel stays faster, against the launch table's choice."""
+    seq = json.load(open(args.seq))
+    pairs = _align(_dispatches(args.csv), seq["launches"])
+    runs, table, dims = {}, {}, {}
+    for (did, sym, row), s in pairs:
+        us = (int(_col(row, "End_Timestamp", "EndNs")) - int(_col(row, "Start_Timestamp", "BeginNs"))) * 1e-3
+        d = runs.setdefault((s["shape"], s["M"], s["kernel"], s["launch"]), [])
+        d.append(us)
+        table[(s["shape"], s["M"])] = s["table_kernel"]
+        dims[s["shape"]] = (s["N"], s["K"])
+    best = {}
+    for (shape, M, kernel, launch), v in runs.items():
+        mean = sum(v) / len(v)
+        cur = best.get((shape, M, kernel))
+        if cur is None or mean < cur[0]:
+            best[(shape, M, kernel)] = (mean, launch, len(v))
+    lines = ["# Switch point: row-vector kernel (VALU dot2) against tiled kernel (MFMA)", "",
+             "command (repository root, after cd /tmp && export TMPDIR=/tmp):", "  " + args.command,
+             "kernel_source_sha256: %s" % seq["kernel_source_sha256"], "",
+             "rocprofv3 kernel-trace durations of bench.py --mode switch: each kernel forced at 1..8",
+             "rows on every matrix shape of the pass, with every launch shape (waves/K slices/slices",
+             "per workgroup) of the table's entries for the matrix that fits at M rows, each launched",
+             "three times on distinct cold copies of the matrix. Per kernel the fastest shape's mean;",
+             "weight GB/s = weight bytes / that mean.", "",
+             "| shape | M | row-vector us (shape) | tiled us (shape) | tiled / row-vector | "
+             "faster | table's kernel | weight GB/s of the faster |",
+             "|---|---|---|---|---|---|---|---|"]
+    shapes = sorted({k[0] for k in best}, key=lambda sh: list(dims).index(sh))
+    agree = True
+    summary = []
+    for shape in shapes:
+        N, K = dims[shape]
+        first = None
+        for M in sorted({k[1] for k in best if k[0] == shape}):
+            v, t = best.get((shape, M, "vector")), best.get((shape, M, "tiled"))
+            if v is None or t is None:
+                continue
+            faster = "tiled" if t[0] < v[0] else "vector"
+            if faster == "tiled" and first is None:
+                first = M
+            elif faster == "vector":
+                first = None
+            if faster != table[(shape, M)]:
+                agree = False
+            gbs = acc.weight_bytes(N, K) / (min(v[0], t[0]) * 1e-6) / 1e9
+            lines.append("| %s | %d | %.3f (%s) | %.3f (%s) | %.3f | %s | %s | %.1f |" % (
+                shape, M, v[0], v[1], t[0], t[1], t[0] / v[0], faster, table[(shape, M)], gbs))
+        summary.append((shape, first))
+    lines += ["", "Row count from which the tiled kernel is faster at every measured M (none: the",
+              "row-vector kernel wins somewhere at the top):", ""]
+    for shape, first in summary:
+        lines.append("switch_point[%s]: %s" % (shape, first if first is not None else "none"))
+    lines.append("table_agrees_with_measurement: %s" % ("yes" if agree else "no"))
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -436,9 +499,14 @@ def main(argv=None):
     kc.add_argument("--command", required=True)
     kc.add_argument("--out", required=True)
     kc.add_argument("--sha", default="")
+    sw = sub.add_parser("switch")
+    sw.add_argument("--csv", required=True)
+    sw.add_argument("--seq", required=True)
+    sw.add_argument("--command", required=True)
+    sw.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     {"trace": trace, "counters": counters, "stats": stats, "pipeline": pipeline,
-     "kernel-counters": kernel_counters}[args.what](args)
+     "kernel-counters": kernel_counters, "switch": switch}[args.what](args)
 
 
 if __name__ == "__main__":

@@ -205,3 +205,61 @@ def test_kernel_counters(tmp_path):
     assert "share of wave time waiting on counters: 0.6" in text  # mean of 2000, 4000 over 5000
     assert "VALU instructions per wave: 30" in text
     assert "VALU active share" not in text  # SQ_ACTIVE_INST_VALU not collected
+
+
+def _switch_seq(table_kernel):
+    # both kernels at 1..4 rows on one shape, two launch shapes each, three launches per shape
+    launches = []
+    N, K = SHAPES["square"]
+    for M in range(1, 5):
+        for kernel in ("vector", "tiled"):
+            sym = "qmm_vector_kernel<%d>" % M if kernel == "vector" else "qmm_tiled_kernel<1, false, 0>"
+            for launch in ("4/2/2", "4/3/1"):
+                for _ in range(3):
+                    launches.append({"symbol": sym, "shape": "square", "M": M, "N": N, "K": K,
+                                     "kernel": kernel, "table_kernel": table_kernel(M),
+                                     "launch": launch})
+    return {"kernel_source_sha256": "0123456789abcdef", "launches": launches}
+
+
+def _switch_us(s):
+    # row-vector: 6 us + 2 us per row; tiled: 9 us flat; the 4/3/1 shape 1 us slower
+    base = 6.0 + 2.0 * s["M"] if s["kernel"] == "vector" else 9.0
+    return base + (1.0 if s["launch"] == "4/3/1" else 0.0)
+
+
+def _write_switch_trace(path, seq):
+    cols = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        t = 1000
+        for did, s in enumerate(seq["launches"], start=1):
+            w.writerow(["KERNEL_DISPATCH", did, "void qmm::%s(qmm::Args)" % s["symbol"], t,
+                        t + int(_switch_us(s) * 1000)])
+            t += 10 ** 6
+
+
+@pytest.mark.parametrize("table_from", [2, 1])
+def test_switch_summary(tmp_path, table_from):
+    # the tiled kernel is faster from 2 rows (8 + 2 = 10 > 9 us); a table that
+    # switches at 1 row disagrees with the measurement at M = 1
+    seq = _switch_seq(lambda M: "tiled" if M >= table_from else "vector")
+    json.dump(seq, open(tmp_path / "seq.json", "w"))
+    _write_switch_trace(tmp_path / "trace.csv", seq)
+    out = tmp_path / "switch.md"
+    ps.main(["switch", "--csv", str(tmp_path / "trace.csv"), "--seq", str(tmp_path / "seq.json"),
+             "--command", "rocprofv3 ... -- python3 bench.py --mode switch", "--out", str(out)])
+    text = out.read_text()
+    rows = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 8 and cells[0] == "square":
+            rows[int(cells[1])] = cells
+    assert sorted(rows) == [1, 2, 3, 4]
+    assert rows[1][2] == "8.000 (4/2/2)" and rows[1][3] == "9.000 (4/2/2)"
+    assert rows[1][5] == "vector" and all(rows[m][5] == "tiled" for m in (2, 3, 4))
+    assert rows[4][4] == "%.3f" % (9.0 / 14.0)
+    assert float(rows[2][7]) == pytest.approx(acc.weight_bytes(5120, 5120) / 9e-6 / 1e9, rel=1e-3)
+    assert "switch_point[square]: 2" in text
+    assert ("table_agrees_with_measurement: yes" in text) == (table_from == 2)
