@@ -10,7 +10,7 @@ Prints one JSON line: weight GB/s over the step (value), ms per pass per M, and
 in the same run: the 32-row pass, a fused-projection pass (each layer's five
 same-input projections as one 25600-row call: 257 calls over the same bytes),
 the four single-matrix workloads per row count, the memory-system probes
-(stream-read ceiling, sustained read, launch gap), per-(shape, M) kernel
+(stream-read ceiling, sustained read, launch gap, shader clock), per-(shape, M) kernel
 durations, the roofline of the dominant kernel and the oracle timed on the
 host cores on a bounded sample.
 
@@ -383,8 +383,9 @@ def probes_measure(torch, acc):
     """The memory system and launch path on their own (include/qmm_probe.h):
     a read-only 128-bit streaming kernel over 4 GiB (best of a few grid
     shapes), the same kernel reading one lm_head-sized buffer back to back for
-    ~100 ms (sustained read), and 513 empty kernels in a graph (the launch gap
-    between back-to-back launches of a pass)."""
+    ~100 ms (sustained read), 513 empty kernels in a graph (the launch gap
+    between back-to-back launches of a pass), and the shader clock the compute
+    units run at (median over workgroups on every CU)."""
     from skinny_bit_block_amd import probe
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -450,6 +451,17 @@ def probes_measure(torch, acc):
     ts.sort()
     out["launch_gap_us"] = round(ts[2], 3)
     del g
+    # shader clock: four 64-thread workgroups per CU, each a dependent FMA chain
+    # between two readings of the clock counter and the constant-rate counter
+    wgs = 1024
+    counts = torch.zeros(4 * wgs, dtype=torch.int64, device="cuda")
+    khz = probe.qmm_probe_clock(counts.data_ptr(), wgs, 1 << 20, sp)
+    torch.cuda.synchronize()
+    c = counts.view(wgs, 4).cpu().numpy().astype("float64")
+    ghz = sorted((c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * khz * 1e-6)
+    out["shader_clock_ghz"] = {"median": round(ghz[wgs // 2], 3), "min": round(ghz[0], 3),
+                               "max": round(ghz[-1], 3), "workgroups": wgs, "wall_clock_khz": khz}
+    del counts
     torch.cuda.empty_cache()
     return out
 

@@ -9,7 +9,8 @@
  * These are the MI355X counterparts: a read-only streaming kernel (the
  * stream-read ceiling on a large buffer, or the sustained read of one
  * matrix) and an empty kernel (the launch gap between back-to-back launches
- * on one stream).
+ * on one stream), plus a shader-clock probe, so that cycle counts and
+ * per-CU rates can be stated at the clock the compute units actually ran.
  */
 #ifndef QMM_PROBE_H
 #define QMM_PROBE_H
@@ -36,6 +37,20 @@ int qmm_probe_read(const void* buf, uint64_t bytes, int grid, int block, uint32_
  * back-to-back launches of it measure the launch gap. Returns 0 or
  * QMM_ERR_INVALID_ARG / QMM_ERR_HIP. */
 int qmm_probe_empty(int grid, hipStream_t stream);
+
+/* Shader clock: `grid` workgroups of 64 threads (1 <= grid <= 2^20) each run
+ * a dependent chain of `iters` fp32 FMAs (1 <= iters <= 2^26), and lane 0 of
+ * workgroup b writes the shader clock counter (s_memtime) and the
+ * constant-rate counter (s_memrealtime) read before and after the chain to
+ * counts[4b], counts[4b+1], counts[4b+2], counts[4b+3] (device memory, 8-byte
+ * aligned, 4 * grid words, owned by the caller). *wall_khz (host memory)
+ * receives the constant counter's rate in kHz (the device attribute
+ * hipDeviceAttributeWallClockRate of the current device), so that a
+ * workgroup's clock is (counts[4b+2] - counts[4b]) / (counts[4b+3] -
+ * counts[4b+1]) * wall_khz kHz. Enqueued on `stream`; the readings are valid
+ * once it has completed. Returns 0 or QMM_ERR_INVALID_ARG / QMM_ERR_ALIGN /
+ * QMM_ERR_HIP. */
+int qmm_probe_clock(uint64_t* counts, int grid, int iters, int* wall_khz, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
-// Measurement probes (include/qmm_probe.h): a read-only streaming kernel and
-// an empty kernel. They run beside the product so that its bandwidth can be
-// stated against what the memory system streams with no arithmetic at all,
-// and its per-call cost against the bare launch gap.
+// Measurement probes (include/qmm_probe.h): a read-only streaming kernel, an
+// empty kernel and a shader-clock probe. They run beside the product so that
+// its bandwidth can be stated against what the memory system streams with no
+// arithmetic at all, its per-call cost against the bare launch gap, and its
+// cycle counts against the clock the compute units actually ran at.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,6 +37,26 @@ __global__ void probe_read(const u4_t* __restrict__ buf, long long n, long long 
 
 __global__ void probe_empty() {}
 
+// Lane 0 of workgroup b reads the shader clock counter (s_memtime) and the
+// constant-rate counter (s_memrealtime) before and after a dependent chain of
+// `iters` fp32 FMAs, and writes the four readings to counts[4b .. 4b+3].
+__global__ void probe_clock(unsigned long long* __restrict__ counts, int iters) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  float a = (float)threadIdx.x;
+  for (int i = 0; i < iters; ++i) a = __builtin_fmaf(a, 0.999999f, 1.0f);
+  asm volatile("" ::"v"(a));  // the chain completes before the second readings
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    unsigned long long* o = counts + 4 * (size_t)blockIdx.x;
+    o[0] = t0;
+    o[1] = r0;
+    o[2] = t1;
+    o[3] = r1;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,6 +75,19 @@ int qmm_probe_read(const void* buf, uint64_t bytes, int grid, int block, uint32_
 int qmm_probe_empty(int grid, hipStream_t stream) {
   if (grid < 1) return QMM_ERR_INVALID_ARG;
   hipLaunchKernelGGL(probe_empty, dim3(grid), dim3(64), 0, stream);
+  return hipGetLastError() == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+int qmm_probe_clock(uint64_t* counts, int grid, int iters, int* wall_khz, hipStream_t stream) {
+  if (!counts || !wall_khz || grid < 1 || grid > (1 << 20) || iters < 1 || iters > (1 << 26))
+    return QMM_ERR_INVALID_ARG;
+  if ((uintptr_t)counts & 7) return QMM_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return QMM_ERR_HIP;
+  hipLaunchKernelGGL(probe_clock, dim3(grid), dim3(64), 0, stream,
+                     reinterpret_cast<unsigned long long*>(counts), iters);
   return hipGetLastError() == hipSuccess ? QMM_OK : QMM_ERR_HIP;
 }
 

@@ -4,7 +4,7 @@ import ctypes
 
 from . import load as _load_lib, _check
 
-EXPORTS = ["qmm_probe_read", "qmm_probe_empty"]
+EXPORTS = ["qmm_probe_read", "qmm_probe_empty", "qmm_probe_clock"]
 
 _done = False
 
@@ -18,6 +18,8 @@ def _lib():
         lib.qmm_probe_read.restype = ctypes.c_int
         lib.qmm_probe_empty.argtypes = [ctypes.c_int, vp]
         lib.qmm_probe_empty.restype = ctypes.c_int
+        lib.qmm_probe_clock.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int), vp]
+        lib.qmm_probe_clock.restype = ctypes.c_int
         _done = True
     return lib
 
@@ -29,3 +31,10 @@ def qmm_probe_read(buf_ptr, nbytes, grid, block, sink_ptr, stream_ptr):
 
 def qmm_probe_empty(grid, stream_ptr):
     return _check(_lib().qmm_probe_empty(int(grid), stream_ptr))
+
+
+def qmm_probe_clock(counts_ptr, grid, iters, stream_ptr):
+    """Launch the clock probe; returns the constant counter's rate in kHz."""
+    khz = ctypes.c_int(0)
+    _check(_lib().qmm_probe_clock(counts_ptr, int(grid), int(iters), ctypes.byref(khz), stream_ptr))
+    return khz.value

@@ -184,3 +184,25 @@ def test_run_ids_argument_checks(planner):
     assert run(planner, 0x10000, 0x20000000, 0x40000000 + 8, 8, 0x40000000, 4, 16, 256, 0) == sbb.QMM_ERR_OVERLAP
     assert run(planner, 0x10000, 0x20000000, 0x30000000, 8, 0x20000000 + 7 * 16 * 144, 4, 16, 256, 0) == sbb.QMM_ERR_OVERLAP
     assert run(planner, *ok) == sbb.QMM_ERR_NO_DEVICE
+
+
+def test_probe_argument_checks():
+    # host-side checks of the probes, before any device call (no GPU needed)
+    from skinny_bit_block_amd import probe
+    lib = probe._lib()
+    vp = ctypes.c_void_p
+    khz = ctypes.c_int(0)
+    fake = vp(0x10000)  # never dereferenced: every call below fails its checks first
+    assert lib.qmm_probe_read(None, 16, 1, 64, fake, None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_read(fake, 16, 0, 64, fake, None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_read(fake, 16, 1, 96, fake, None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_read(vp(0x10008), 16, 1, 64, fake, None) == sbb.QMM_ERR_ALIGN
+    assert lib.qmm_probe_read(fake, 24, 1, 64, fake, None) == sbb.QMM_ERR_ALIGN
+    assert lib.qmm_probe_empty(0, None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(None, 1, 1, ctypes.byref(khz), None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(fake, 1, 1, None, None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(fake, 0, 1, ctypes.byref(khz), None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(fake, (1 << 20) + 1, 1, ctypes.byref(khz), None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(fake, 1, 0, ctypes.byref(khz), None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(fake, 1, (1 << 26) + 1, ctypes.byref(khz), None) == sbb.QMM_ERR_INVALID_ARG
+    assert lib.qmm_probe_clock(vp(0x10004), 1, 1, ctypes.byref(khz), None) == sbb.QMM_ERR_ALIGN
