@@ -1,5 +1,6 @@
-"""A seeded sweep of forced launch shapes over ragged small matrices on the GPU,
-in the three weight formats, against the binary64 oracles.
+"""Seeded sweeps of forced launch shapes over ragged small matrices on the GPU,
+in the three weight formats and for expert-indexed calls, against the
+binary64 oracles.
 
 The cases are drawn the way the host address replay draws its own seeded
 sweep (tests/test_address_sim.py): N with ragged last row tiles, K of 1..17
@@ -119,3 +120,85 @@ def test_forced_shape_sweep(h, i):
     bad = err > TOL * aref
     assert not bad.any(), "%s: %d of %d outside the gate, worst err/A %.3g" % (
         what, int(bad.sum()), bad.size, float((err / np.maximum(aref, 1e-300)).max()))
+
+
+# ------------------------------------------------------------- expert-indexed
+
+ID_KINDS = ["random", "same", "distinct", "invalid"]
+NIDS = 150
+_id_cases = []
+
+
+def id_pattern(kind, M, E, rng):
+    if kind == "random":
+        return rng.integers(0, E, M)
+    if kind == "same":
+        return np.full(M, int(rng.integers(0, E)))
+    if kind == "distinct":
+        return rng.permutation(E)[:M] if M <= E else np.arange(M) % E
+    v = rng.integers(0, E, M)  # invalid ids (negative, past E) write nothing
+    v[::3] = -1
+    if M > 1:
+        v[1] = E + 5
+    return v
+
+
+def draw_id_cases(n=NIDS, seed=20261204):
+    """(M, N, K, E, ids, (waves, splits, grid), wsplit) that the planner accepts
+    for an expert-indexed call (slots = min(M, E))."""
+    rng = np.random.default_rng(seed)
+    h = sbb.qmm_create(sbb.QMM_DEVICE_NONE)
+    out = []
+    try:
+        while len(out) < n:
+            N, K = int(rng.choice(NS)), int(rng.choice(KS[:9]))
+            M = int(rng.integers(1, 33))
+            E = int(rng.choice([1, 2, 3, 5, 8, 17]))
+            ids = id_pattern(str(rng.choice(ID_KINDS)), M, E, rng).astype(np.int32)
+            shape = (int(rng.integers(1, 9)), int(rng.integers(0, K // 256 + 1)),
+                     int(rng.choice([0, 0, 1, 2, 3, 7])))
+            wsplit = int(rng.choice([0, 1, 1, 2, 3, 4, 8]))
+            if addr.plan(h, sbb.FORMAT_KQUANT, min(M, E), M, N, K, sbb.KERNEL_AUTO, shape,
+                         wsplit) is not None:
+                out.append((M, N, K, E, ids, shape, wsplit))
+    finally:
+        sbb.qmm_destroy(h)
+    return out
+
+
+def id_cases():
+    if not _id_cases:
+        _id_cases.extend(draw_id_cases())
+    return _id_cases
+
+
+@pytest.mark.parametrize("i", range(NIDS))
+def test_expert_indexed_sweep(h, i):
+    M, N, K, E, ids, shape, wsplit = id_cases()[i]
+    what = "M=%d N=%d K=%d E=%d ids=%s shape=%s wsplit=%d" % (M, N, K, E, ids.tolist(), shape, wsplit)
+    tensor = 9000 + 40 * i
+    x = synth.acts(M, K, tensor=tensor, seed=SEED)
+    W = np.concatenate([synth.weights(N, K, tensor=tensor + 1 + e, seed=SEED).reshape(-1)
+                        for e in range(E)])
+    yref, aref, written = oracle.qmm_ids(x, W, ids, E, N, K)
+    sbb.qmm_set_shape(h, *shape)
+    sbb.qmm_set_wave_splits(h, wsplit)
+    try:
+        p = sbb.qmm_query_plan_format(h, sbb.FORMAT_KQUANT, min(M, E), M, N, K)
+        # each slot stages the rows of one expert: every row count up to M
+        for m in sorted({1, M} | {int((ids == e).sum()) for e in range(E) if (ids == e).any()}):
+            addr.replay(p, m, N, K)
+        xd, Wd = dev(x), dev(W)
+        idd = torch.from_numpy(ids).cuda()
+        y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+        sbb.qmm_run_ids(h, xd, Wd, idd, E, y, M, N, K)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+    finally:
+        sbb.qmm_set_shape(h, 0, 0, 0)
+        sbb.qmm_set_wave_splits(h, 0)
+    assert np.all(y[~written] == 7.0), what + ": a row with an invalid id was written"
+    yw = y[written].astype(np.float64)
+    assert np.isfinite(yw).all(), what
+    bad = np.abs(yw - yref[written]) > TOL * aref[written]
+    assert not bad.any(), "%s: %d elements outside the gate" % (what, int(bad.sum()))
