@@ -182,3 +182,37 @@ def test_graph_replays_match_eager_calls():
         assert torch.equal(st_g, st_e), step
         st_e.add_(0.0)  # eager work between replays
     assert not torch.equal(st_g.cpu(), torch.from_numpy(state))  # the commits moved it
+
+
+def draw_gdn_cases(n=80, seed=20261205):
+    """Seeded (B, H, L, M, n_log, commit, gate regime) cases: ragged and
+    out-of-range log counts and commits, empty logs and calls without new
+    rows, and ordinary, tiny and zero gates."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, H = int(rng.integers(1, 6)), int(rng.integers(1, 4))
+        L, M = int(rng.choice([0, 1, 3, 8, 20])), int(rng.choice([0, 1, 2, 4, 7]))
+        n_log = [int(v) for v in rng.integers(-2, L + 3, B)] if L > 0 else None
+        commit = [int(v) for v in rng.integers(-2, L + M + 3, B)] if rng.random() < 0.8 else None
+        out.append((B, H, L, M, n_log, commit, str(rng.choice(["plain", "plain", "small", "zero"]))))
+    return out
+
+
+GDN_CASES = draw_gdn_cases()
+
+
+@pytest.mark.parametrize("i", range(len(GDN_CASES)))
+def test_seeded_sweep(i):
+    B, H, L, M, n_log, commit, gates = GDN_CASES[i]
+    state, log, new = make(B, H, L, M, tensor=1000 + 10 * i)
+    for d in (log, new):
+        if d is None:
+            continue
+        if gates == "small":
+            d["gate"][:] = 1e-3
+        elif gates == "zero":
+            d["gate"][:, ::2] = 0.0
+    st, o = run(state, log, n_log, new, commit, B, H, M)
+    check(state, log, n_log, new, commit, st, o,
+          "sweep %d: B=%d H=%d L=%d M=%d n_log=%s commit=%s gates=%s" % (i, B, H, L, M, n_log, commit, gates))
