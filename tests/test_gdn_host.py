@@ -78,3 +78,59 @@ def test_call_bytes():
         32 * 4 * 48 * (2 * 128 + 128 + 2) * 4 + 32 * 4 * 48 * 128 * 4
     assert got == want
     assert gdn.gdn_call_bytes(-1, 4, 48, 128, 128, 0, 0) == 0
+
+
+# ------------------------------------------------- overlap rule, property-based
+
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+NAMES = ["state", "k_log", "v_log", "gate_log", "beta_log", "n_log", "q", "k", "v", "gate", "beta",
+         "commit", "o"]
+INPUTS = NAMES[1:12]
+
+
+def extents(Bn, Hn, Ln, Mn, with_commit):
+    """Bytes of every array of a call, as the header documents them."""
+    lrow, nrow = Bn * Ln * Hn, Bn * Mn * Hn
+    e = {"state": Bn * Hn * D * D * 4, "k_log": lrow * D * 4, "v_log": lrow * D * 4,
+         "gate_log": lrow * 4, "beta_log": lrow * 4, "n_log": Bn * 4 if Ln else 0,
+         "q": nrow * D * 4, "k": nrow * D * 4, "v": nrow * D * 4, "gate": nrow * 4,
+         "beta": nrow * 4, "commit": Bn * 4 if with_commit else 0, "o": nrow * D * 4}
+    return e
+
+
+def meets(a, na, b, nb):
+    return na > 0 and nb > 0 and a < b + nb and b < a + na
+
+
+@settings(max_examples=600, deadline=None, derandomize=True)
+@given(data=st.data())
+def test_overlap_rule(data):
+    # arrays placed at random, often on top of one another: the call reports
+    # QMM_ERR_ALIGN for a misaligned pointer, else QMM_ERR_OVERLAP exactly when
+    # the state meets any other array or o meets an input, else it reaches the
+    # device query (inputs may share memory with one another)
+    Bn, Hn = data.draw(st.integers(1, 3)), data.draw(st.integers(1, 3))
+    Ln, Mn = data.draw(st.integers(0, 3)), data.draw(st.integers(0, 3))
+    with_commit = data.draw(st.booleans())
+    ext = extents(Bn, Hn, Ln, Mn, with_commit)
+    used = [n for n in NAMES if ext[n] > 0]
+    slots = data.draw(st.lists(st.integers(0, 11), min_size=len(used), max_size=len(used)))
+    offs = data.draw(st.lists(st.integers(0, 1 << 17), min_size=len(used), max_size=len(used)))
+    misalign = data.draw(st.sampled_from(used)) if data.draw(st.integers(0, 9)) == 0 else None
+    ptr = {n: None for n in NAMES}
+    for n, s, o in zip(used, slots, offs):
+        ptr[n] = BASE + s * (1 << 22) + 4 * o + (2 if n == misalign else 0)
+    a = dict(state=ptr["state"], L=Ln, B=Bn, M=Mn, H=Hn, dk=D, dv=D,
+             **{n: ptr[n] for n in NAMES[1:]})
+    got = call(**a)
+    if misalign is not None:
+        assert got == sbb.QMM_ERR_ALIGN, (a, got)
+        hypothesis.event("misaligned")
+        return
+    clash = any(meets(ptr["state"], ext["state"], ptr[n], ext[n]) for n in NAMES[1:] if ptr[n]) or \
+        any(meets(ptr["o"], ext["o"], ptr[n], ext[n]) for n in INPUTS if ptr[n] and ptr["o"])
+    hypothesis.event("overlap" if clash else "disjoint")
+    assert got == (sbb.QMM_ERR_OVERLAP if clash else sbb.QMM_ERR_NO_DEVICE), (a, got, clash)
