@@ -23,7 +23,8 @@ HIPCC = lib_build.HIPCC
 
 # the CPU tests that call into the library's host code / the oracle's C code
 LIBRARY_TESTS = ["tests/test_abi.py", "tests/test_plan_table.py", "tests/test_gdn_host.py",
-                 "tests/test_int4_host.py", "tests/test_nvfp4_host.py"]
+                 "tests/test_int4_host.py", "tests/test_nvfp4_host.py", "tests/test_plan_properties.py",
+                 "tests/test_run_properties.py"]
 ORACLE_TESTS = ["tests/test_oracle.py", "tests/test_oracle_ids.py"]
 REPORTS = ("ERROR: AddressSanitizer", "runtime error:", "ERROR: LeakSanitizer")
 
