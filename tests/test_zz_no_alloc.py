@@ -5,7 +5,8 @@ compared bitwise with qmm_run on a fresh handle (same launch plan, same
 kernels) and with the oracle at the product's gate; both calls use split-K
 across workgroups, so the static scratch (partial sums and arrival
 counters) is what they run on. A plan too large for the scratch is refused
-with QMM_ERR_SCRATCH and writes nothing.
+with QMM_ERR_SCRATCH and writes nothing. A seeded sequence of 60 small
+ragged calls, most of them split-K, runs on the same scratch one after another.
 """
 import numpy as np
 import pytest
@@ -68,3 +69,43 @@ def test_static_entry_refuses_oversized_plans():
     assert rc == sbb.QMM_ERR_SCRATCH
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+def test_static_entry_seeded_sequence():
+    # 60 calls in a row on small ragged matrices: their automatic plans split K
+    # across workgroups heavily, so each call reuses the static partials and
+    # the arrival counters the previous one left (which must be back at zero);
+    # every call matches qmm_run bitwise and the oracle at the gate, and every
+    # plan's loads are replayed on the host first
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import test_address_sim as addr
+    rng = np.random.default_rng(20261206)
+    h = sbb.qmm_create(0)
+    s = torch.cuda.current_stream().cuda_stream
+    split_k = 0
+    try:
+        for i in range(60):
+            M = int(rng.integers(1, 33))
+            N = int(rng.choice([1, 3, 16, 17, 33, 100, 257, 1000, 2047]))
+            K = 256 * int(rng.integers(1, 18))
+            p = sbb.qmm_query_plan(h, M, N, K)
+            addr.replay(p, M, N, K)
+            split_k += p["workspace_bytes"] > 0
+            x, W = _case(M, N, K, 100 + i)
+            xd = torch.from_numpy(x).cuda()
+            Wd = torch.from_numpy(W.reshape(-1)).cuda()
+            ys = torch.full((M, N), np.nan, dtype=torch.float32, device="cuda")
+            yr = torch.full((M, N), np.nan, dtype=torch.float32, device="cuda")
+            rc = sbb.qmm_run_static_raw(xd.data_ptr(), Wd.data_ptr(), ys.data_ptr(), M, N, K, s)
+            assert rc == sbb.QMM_OK, (i, M, N, K, sbb.qmm_status_string(rc))
+            sbb.qmm_run(h, xd, Wd, yr, M, N, K)
+            torch.cuda.synchronize()
+            a, b = ys.cpu().numpy(), yr.cpu().numpy()
+            what = "call %d: M=%d N=%d K=%d" % (i, M, N, K)
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
+            yref, aref = oracle.qmm(x, W, N, K)
+            assert np.all(np.abs(a.astype(np.float64) - yref) <= 2e-3 * aref), what
+    finally:
+        sbb.qmm_destroy(h)
+    assert split_k >= 30  # most of the sequence runs on the static split-K scratch
