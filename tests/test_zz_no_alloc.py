@@ -6,7 +6,8 @@ kernels) and with the oracle at the product's gate; both calls use split-K
 across workgroups, so the static scratch (partial sums and arrival
 counters) is what they run on. A plan too large for the scratch is refused
 with QMM_ERR_SCRATCH and writes nothing. A seeded sequence of 60 small
-ragged calls, most of them split-K, runs on the same scratch one after another.
+ragged calls, most of them split-K, runs on the same scratch one after another,
+and a captured HIP graph of such calls replays bitwise like the eager calls.
 """
 import numpy as np
 import pytest
@@ -109,3 +110,48 @@ def test_static_entry_seeded_sequence():
     finally:
         sbb.qmm_destroy(h)
     assert split_k >= 30  # most of the sequence runs on the static split-K scratch
+
+
+def test_static_entry_in_a_graph():
+    # the use the entry point is for: calls captured into a HIP graph. The
+    # first call on the device (its set-up) is made before the capture, as a
+    # warm-up; then the captured sequence is replayed four times with eager
+    # calls on the same scratch and synchronizations in between, and every
+    # replay must equal the eager results bitwise
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cases = [(8, 5120, 17408), (4, 1000, 2560), (1, 300, 4352), (32, 2047, 1280)]
+    bufs = []
+    for i, (M, N, K) in enumerate(cases):
+        x, W = _case(M, N, K, 300 + i)
+        bufs.append((M, N, K, torch.from_numpy(x).cuda(), torch.from_numpy(W.reshape(-1)).cuda(),
+                     torch.full((M, N), np.nan, dtype=torch.float32, device="cuda")))
+
+    def run(stream, outs):
+        for (M, N, K, xd, Wd, _), y in zip(bufs, outs):
+            rc = sbb.qmm_run_static_raw(xd.data_ptr(), Wd.data_ptr(), y.data_ptr(), M, N, K, stream)
+            assert rc == sbb.QMM_OK, sbb.qmm_status_string(rc)
+
+    eager = [torch.full_like(b[5], np.nan) for b in bufs]
+    run(torch.cuda.current_stream().cuda_stream, eager)  # warm-up and reference
+    torch.cuda.synchronize()
+    graph_out = [b[5] for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        run(side.cuda_stream, graph_out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for y in graph_out:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (y, e) in enumerate(zip(graph_out, eager)):
+            assert torch.equal(y.view(torch.int32), e.view(torch.int32)), "replay %d, call %d" % (rep, i)
+        again = [torch.full_like(e, np.nan) for e in eager]  # eager work on the same scratch
+        run(torch.cuda.current_stream().cuda_stream, again)
+        torch.cuda.synchronize()
+        for i, (a, e) in enumerate(zip(again, eager)):
+            assert torch.equal(a.view(torch.int32), e.view(torch.int32)), "eager %d, call %d" % (rep, i)
